@@ -1,0 +1,133 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) routed-expert MoE FFN layer library
+ * (libmoe.so).
+ *
+ * The layer, for every token t of x[T, H]:
+ *   1. router: logits l = x_t . router_w^T (+ router_bias), accumulated in
+ *      fp32 and never rounded to bf16; the top_k experts by logit (descending,
+ *      ties to the lower expert index); weights w = softmax of the k selected
+ *      logits (equal to the full softmax renormalised over the selection).
+ *      Pages: "MoE prefill quantum" (cause section: each token uses k of E
+ *      experts); "DeepSeek V4.1F Q4 with native DSpark MTP" (decode
+ *      paragraph: the router as a single fused dispatch).
+ *   2. permutation: the (t, j) pairs grouped by expert, stably (t, then j
+ *      ascending within an expert).
+ *   3. per expert e: h = silu(x W_gate[e]^T) * (x W_up[e]^T)  (SwiGLU with the
+ *      SiLU on the gate branch; "Jetson Orin Nano MoE ... expert cache",
+ *      re-check section and gate-first section).
+ *   4. o = h W_down[e]^T, scaled by w[t, j]; y_t = sum over j = 0..k-1 of the
+ *      scaled rows in that fixed order (same page, nondeterminism section:
+ *      each expert owns its output rows, so the order of the sum is fixed),
+ *      plus, if present, the always-on shared expert's output with weight 1
+ *      ("DeepSeek V4.1F" decode paragraph).
+ *
+ * Layouts (row-major, K-contiguous):
+ *   x [T, H], y [T, H]              act_dtype (MOE_F32 or MOE_BF16)
+ *   router_w [E, H]                 act_dtype
+ *   router_bias [E]                 float, or NULL
+ *   w_gate, w_up [E, I, H]          w_dtype
+ *   w_down [E, H, I]                w_dtype
+ *     MXFP4 (OCP MX v1.0): codes [E, I, H/2] / [E, H, I/2], two E2M1 codes
+ *     per byte, even element in the low nibble; s_* E8M0 scales
+ *     [E, I, H/32] / [E, H, I/32], one per 32 consecutive K elements.
+ *   sh_gate, sh_up [I_shared, H], sh_down [H, I_shared]   act_dtype
+ *   topk_idx [T, top_k] int32, topk_w [T, top_k] float
+ *
+ * Supported combinations: act F32 with w F32; act BF16 with w BF16 or MXFP4.
+ * Every pointer except router_bias, topk_w and the unused ones is a device
+ * pointer, 16-byte aligned.  The caller owns all memory; the library
+ * allocates nothing per call and keeps no state between calls other than
+ * cached device properties.  Calls are asynchronous on `stream` (a
+ * hipStream_t, NULL = the default stream): outputs are valid once the stream
+ * has synchronised.  Nothing is read back to the host inside a call.
+ *
+ * Error handling: every entry point returns MOE_OK (0) or a negative code;
+ * no exception crosses the boundary.  On MOE_EINVAL / MOE_EWORKSPACE nothing
+ * has been launched.  On MOE_EHIP a launch failed; moe_last_error() gives the
+ * HIP error text of the calling thread's last failure.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype_t;
+
+enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,       /* null/misaligned pointer, bad size or dtype  */
+    MOE_EWORKSPACE = -2,   /* ws_bytes < moe_workspace_bytes(shape)       */
+    MOE_EUNSUPPORTED = -3, /* device is not gfx950, or dtype combination  */
+    MOE_EHIP = -4          /* HIP launch/runtime error                    */
+};
+
+typedef struct {
+    int32_t T;         /* tokens                                             */
+    int32_t H;         /* hidden size (multiple of 64)                       */
+    int32_t E;         /* routed experts, 1..1023                            */
+    int32_t top_k;     /* experts per token, 1..min(E, 16)                   */
+    int32_t I;         /* expert intermediate size (multiple of 64)          */
+    int32_t I_shared;  /* shared expert intermediate size, 0 = none          */
+    int32_t chunk_T;   /* tokens per internal pass, 0 = all T at once        */
+    int32_t act_dtype; /* moe_dtype_t of x, y, router_w and shared weights   */
+    int32_t w_dtype;   /* moe_dtype_t of the routed expert weights           */
+} moe_shape_t;
+
+typedef struct {
+    const void *router_w;
+    const float *router_bias;                /* nullable                     */
+    const void *w_gate, *w_up, *w_down;      /* codes when w_dtype == MXFP4  */
+    const uint8_t *s_gate, *s_up, *s_down;   /* E8M0, MXFP4 only             */
+    const void *sh_gate, *sh_up, *sh_down;   /* I_shared > 0 only            */
+} moe_weights_t;
+
+/* Bytes of device workspace moe_forward / moe_route need for `shape`
+ * (sized for one chunk of min(T, chunk_T) tokens); 0 if the shape is
+ * invalid. */
+size_t moe_workspace_bytes(const moe_shape_t *shape);
+
+/* The whole layer: y [T, H] and the routing (topk_idx required, topk_w
+ * nullable).  `ws` is device memory of at least moe_workspace_bytes(shape)
+ * bytes, 256-byte aligned, owned by the caller; its contents on entry do not
+ * matter.  The result does not depend on chunk_T beyond rounding order: each
+ * chunk is processed independently in token order. */
+int moe_forward(const moe_shape_t *shape, const moe_weights_t *w,
+                const void *x, void *y, int32_t *topk_idx, float *topk_w,
+                void *ws, size_t ws_bytes, void *stream);
+
+/* Router and permutation only (analysis / test export).  For the tokens of
+ * one pass (chunk_T must be 0 or >= T): topk_idx [T, k], topk_w [T, k],
+ * counts [E] (pairs per expert), offsets [E+1] (exclusive prefix of counts)
+ * and row_src [T*k] (the pair t*k+j at each grouped position).  All device
+ * pointers; topk_w, counts, offsets and row_src are nullable. */
+int moe_route(const moe_shape_t *shape, const moe_weights_t *w,
+              const void *x, int32_t *topk_idx, float *topk_w,
+              int32_t *counts, int32_t *offsets, int32_t *row_src,
+              void *ws, size_t ws_bytes, void *stream);
+
+/* Stage timing for measurement (not needed for computing).  While enabled,
+ * moe_forward records a pair of HIP events on its stream around each of its
+ * stages - 0 router, 1 permutation, 2 gate+up, 3 down, 4 combine - for up to
+ * 4096 calls; moe_stage_timing_read waits for them, writes the summed
+ * milliseconds per stage into ms[0..n_stages) and the number of recorded
+ * calls into *n_calls, and clears the record.  Enabling or disabling also
+ * clears it.  Process-wide; returns MOE_OK or MOE_EHIP. */
+int moe_stage_timing_enable(int on);
+int moe_stage_timing_read(float *ms, int n_stages, int *n_calls);
+
+/* Static text for a return code. */
+const char *moe_strerror(int code);
+
+/* Detail of the calling thread's last failure (argument name or HIP error). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,169 @@
+"""Python binding of libmoe.so, the gfx950 routed-expert MoE FFN layer.
+
+Argument marshalling only: torch tensors are passed by device pointer and
+every step of the layer runs in the library's HIP kernels.  The functions
+carry the names of the C entry points declared in ``include/moe.h``.
+
+The library must have been built (``python -m routed_expert_ffn_moe_amd.build``);
+importing the binding does not build it, and every call fails loudly when the
+library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_OK", "MOE_EINVAL", "MOE_EWORKSPACE",
+    "MOE_EUNSUPPORTED", "MOE_EHIP", "MoeError", "moe_shape_t", "moe_weights_t", "make_shape",
+    "make_weights", "moe_workspace_bytes", "moe_forward", "moe_route", "moe_strerror",
+    "moe_last_error", "moe_stage_timing_enable", "moe_stage_timing_read", "STAGES",
+    "lib_path", "load",
+]
+
+MOE_F32, MOE_BF16, MOE_MXFP4 = 0, 1, 2
+MOE_OK, MOE_EINVAL, MOE_EWORKSPACE, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3, -4
+_DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp4": MOE_MXFP4}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libmoe.so")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, detail: str):
+        super().__init__("%s (%d): %s" % (moe_strerror(code), code, detail))
+        self.code = code
+
+
+class moe_shape_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("T", "H", "E", "top_k", "I", "I_shared", "chunk_T", "act_dtype", "w_dtype")]
+
+
+class moe_weights_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("router_w", "router_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up",
+                 "s_down", "sh_gate", "sh_up", "sh_down")]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError("libmoe.so is not built: run `python -m routed_expert_ffn_moe_amd.build`")
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        lib.moe_workspace_bytes.restype = ctypes.c_size_t
+        lib.moe_workspace_bytes.argtypes = [P]
+        lib.moe_forward.restype = ctypes.c_int
+        lib.moe_forward.argtypes = [P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.moe_route.restype = ctypes.c_int
+        lib.moe_route.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.moe_strerror.restype = ctypes.c_char_p
+        lib.moe_strerror.argtypes = [ctypes.c_int]
+        lib.moe_last_error.restype = ctypes.c_char_p
+        lib.moe_last_error.argtypes = []
+        lib.moe_stage_timing_enable.restype = ctypes.c_int
+        lib.moe_stage_timing_enable.argtypes = [ctypes.c_int]
+        lib.moe_stage_timing_read.restype = ctypes.c_int
+        lib.moe_stage_timing_read.argtypes = [P, ctypes.c_int, P]
+        _lib = lib
+    return _lib
+
+
+def _ptr(t) -> Optional[int]:
+    """Device pointer of a tensor (None -> NULL; ints pass through)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_shape(T, H, E, top_k, I, I_shared=0, chunk_T=0, act="bf16", w="bf16") -> moe_shape_t:
+    return moe_shape_t(T, H, E, top_k, I, I_shared, chunk_T, _DT[act], _DT[w])
+
+
+class _Weights:
+    """moe_weights_t plus references keeping the tensors alive."""
+
+    def __init__(self, **tensors):
+        self._keep = tensors
+        self.c = moe_weights_t(**{k: _ptr(v) for k, v in tensors.items()})
+
+
+def make_weights(router_w, w_gate, w_up, w_down, router_bias=None, s_gate=None, s_up=None,
+                 s_down=None, sh_gate=None, sh_up=None, sh_down=None) -> _Weights:
+    return _Weights(router_w=router_w, router_bias=router_bias, w_gate=w_gate, w_up=w_up,
+                    w_down=w_down, s_gate=s_gate, s_up=s_up, s_down=s_down, sh_gate=sh_gate,
+                    sh_up=sh_up, sh_down=sh_down)
+
+
+def _check(rc: int):
+    if rc != MOE_OK:
+        raise MoeError(rc, moe_last_error())
+
+
+def moe_workspace_bytes(shape: moe_shape_t) -> int:
+    return int(load().moe_workspace_bytes(ctypes.byref(shape)))
+
+
+def moe_forward(shape, weights, x, y, topk_idx, topk_w, ws, ws_bytes=None, stream=None) -> None:
+    """y[T,H] and the routing of x[T,H]; asynchronous on `stream`."""
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().moe_forward(ctypes.byref(shape), ctypes.byref(weights.c), _ptr(x), _ptr(y),
+                              _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws_bytes,
+                              _stream(stream)))
+
+
+def moe_route(shape, weights, x, topk_idx, topk_w, counts, offsets, row_src, ws, ws_bytes=None,
+              stream=None) -> None:
+    """Router and permutation of one pass (see include/moe.h)."""
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().moe_route(ctypes.byref(shape), ctypes.byref(weights.c), _ptr(x),
+                            _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets),
+                            _ptr(row_src), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+STAGES = ("router", "permute", "gate_up", "down", "combine")
+
+
+def moe_stage_timing_enable(on: bool) -> None:
+    _check(load().moe_stage_timing_enable(1 if on else 0))
+
+
+def moe_stage_timing_read():
+    """(milliseconds summed per stage as a dict, number of timed calls)."""
+    ms = (ctypes.c_float * len(STAGES))()
+    n = ctypes.c_int(0)
+    _check(load().moe_stage_timing_read(ms, len(STAGES), ctypes.byref(n)))
+    return dict(zip(STAGES, [float(v) for v in ms])), n.value
+
+
+def moe_strerror(code: int) -> str:
+    return load().moe_strerror(code).decode()
+
+
+def moe_last_error() -> str:
+    return load().moe_last_error().decode()

@@ -1,0 +1,64 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
+typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+#define MOE_WAVE 64
+
+namespace moe {
+
+// bf16 <-> fp32.  bf16 values travel as uint16_t bit patterns.
+__device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (inputs here are finite).
+__device__ __forceinline__ uint16_t f2bf(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b)
+{
+    return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// Token row and routing weight of a grouped row.  Pairs p < n_pairs are the
+// routed (t, j) pairs p = t * k + j; p >= n_pairs are shared-expert rows of
+// token p - n_pairs.
+__device__ __forceinline__ int pair_token(int p, int n_pairs, int k)
+{
+    return p < n_pairs ? p / k : p - n_pairs;
+}
+
+// MFMA wrappers (operand/result lane layouts verified on gfx950):
+//  16x16x32 bf16: lane l holds A[l%16][8*(l/16) + i], B[k = 8*(l/16) + i][n = l%16],
+//                 C[4*(l/16) + i][l%16].
+__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v)
+{
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// Tile descriptor written by the permutation: group g (expert, or E for the
+// shared expert) and the first grouped row of the tile.
+struct Tile {
+    int g;
+    int row0;
+};
+
+}  // namespace moe

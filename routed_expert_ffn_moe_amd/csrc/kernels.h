@@ -1,0 +1,85 @@
+// Launchers of the gfx950 kernels, called by the host orchestration in
+// moe_api.cpp.  All pointers are device pointers; every launcher is
+// asynchronous on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace moe {
+
+enum { ACT_F32 = 0, ACT_BF16 = 1 };
+enum { W_F32 = 0, W_BF16 = 1, W_MXFP4 = 2 };
+
+struct RouterArgs {
+    const void *x;        // [T, H] act
+    const void *wr;       // [E, H] act
+    const float *bias;    // [E] or null
+    float *logits;        // [T, E] workspace
+    int32_t *idx;         // [T, k]
+    float *w;             // [T, k]
+    int T, H, E, k, act;
+};
+void launch_router(const RouterArgs &a, hipStream_t st);
+
+// Permutation of one pass: counts, offsets and the grouped order of the
+// (t, j) pairs, plus the GEMM tile lists.  Group E is the shared expert
+// (all T tokens, in token order) when `shared` is set.
+struct PermuteArgs {
+    const int32_t *idx;   // [T, k]
+    int32_t *blk;         // [nblk, E] workspace
+    int32_t *counts;      // [E + 1]
+    int32_t *offsets;     // [E + 2]
+    int32_t *row_src;     // [T*k + T]
+    Tile *tiles_a;        // tile list for row-block size bm_a
+    int32_t *ntiles_a;
+    Tile *tiles_b;        // tile list for row-block size bm_b
+    int32_t *ntiles_b;
+    int bm_a, bm_b;
+    int T, E, k, shared;
+};
+int permute_blocks(int n_pairs);  // number of histogram blocks
+void launch_permute(const PermuteArgs &a, hipStream_t st);
+
+// Grouped gate+up GEMM with the SwiGLU epilogue: h[row] = silu(x_t Wg^T) *
+// (x_t Wu^T) for every grouped row; and the grouped down GEMM with the
+// routing-weight scale writing stage[pair].
+struct ExpertArgs {
+    const void *x;                           // [T, H] act
+    const void *w_gate, *w_up, *w_down;      // routed weights (codes for MXFP4)
+    const uint8_t *s_gate, *s_up, *s_down;   // MXFP4 scales
+    const void *sh_gate, *sh_up, *sh_down;   // shared expert (act dtype)
+    const int32_t *row_src;                  // [rows]
+    const int32_t *offsets;                  // [E + 2]
+    const float *topk_w;                     // [T*k]
+    void *h;                                 // [rows, max(I, I_shared)] act
+    void *stage;                             // [rows, H] act
+    const Tile *tiles_gu;
+    const int32_t *ntiles_gu;
+    const Tile *tiles_dc;
+    const int32_t *ntiles_dc;
+    int max_tiles_gu, max_tiles_dc;
+    int T, H, E, k, I, I_shared, act, wdt;
+    int shape_T;  // tokens of a full pass: selects the tile shape
+};
+void launch_gate_up(const ExpertArgs &a, hipStream_t st);
+void launch_down(const ExpertArgs &a, hipStream_t st);
+int gemm_bm_gu(const ExpertArgs &a);  // row-block sizes of the tile lists
+int gemm_bm_dc(const ExpertArgs &a);
+
+// MXFP4 expert weights (bf16 activations, no shared expert).
+int mxfp4_bm();
+void launch_gate_up_mxfp4(const ExpertArgs &a, hipStream_t st);
+void launch_down_mxfp4(const ExpertArgs &a, hipStream_t st);
+
+// y[t] = sum_j stage[t*k + j] (+ stage[T*k + t]) in j order.
+struct CombineArgs {
+    const void *stage;
+    void *y;
+    int T, H, k, shared, act;
+};
+void launch_combine(const CombineArgs &a, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,134 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/moe.h declares, sizes workspaces, and rejects bad arguments with the
+documented codes before touching any device (every case below carries at
+least one argument error, so no kernel is ever launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import routed_expert_ffn_moe_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.load()
+    names = _declared()
+    assert {"moe_forward", "moe_route", "moe_workspace_bytes", "moe_strerror",
+            "moe_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_strerror_codes():
+    assert moe.moe_strerror(0) == "ok"
+    for code in (moe.MOE_EINVAL, moe.MOE_EWORKSPACE, moe.MOE_EUNSUPPORTED, moe.MOE_EHIP):
+        assert moe.moe_strerror(code) not in ("ok", "unknown error code")
+    assert moe.moe_strerror(12345) == "unknown error code"
+
+
+GOOD = dict(T=128, H=2048, E=256, top_k=8, I=768, I_shared=0, chunk_T=0, act="bf16", w="bf16")
+
+
+def shape(**kw):
+    d = dict(GOOD, **kw)
+    return moe.make_shape(d["T"], d["H"], d["E"], d["top_k"], d["I"], d["I_shared"],
+                          d["chunk_T"], d["act"], d["w"])
+
+
+def test_workspace_bytes():
+    n1 = moe.moe_workspace_bytes(shape())
+    assert n1 > 0
+    # chunking bounds the workspace by the pass size
+    assert moe.moe_workspace_bytes(shape(T=4096, chunk_T=128)) == n1
+    assert moe.moe_workspace_bytes(shape(T=4096)) > n1
+    # h and staging rows: T*k bf16 rows of I and H, at least
+    assert n1 >= 128 * 8 * (768 + 2048) * 2
+    assert moe.moe_workspace_bytes(shape(T=0)) >= 0
+    for bad in (dict(H=100), dict(E=0), dict(top_k=9, E=8), dict(I=0), dict(act="f32")):
+        assert moe.moe_workspace_bytes(shape(**bad)) == 0, bad
+
+
+class FakeW:
+    """moe_weights_t with fake (never dereferenced) 256-aligned addresses."""
+
+    def __init__(self, **over):
+        base = 0x7F0000000000
+        d = dict(router_w=base, w_gate=base + 0x1000, w_up=base + 0x2000, w_down=base + 0x3000)
+        d.update(over)
+        self.c = moe.moe_weights_t(**d)
+
+
+def call(sh, w=None, x=0x7F1000000000, y=0x7F2000000000, idx=0x7F3000000000, tw=None,
+         ws=0x7F4000000000, ws_bytes=0):
+    lib = moe.load()
+    w = w or FakeW()
+    return lib.moe_forward(ctypes.byref(sh) if sh is not None else None, ctypes.byref(w.c),
+                           x, y, idx, tw, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(T=-1), moe.MOE_EINVAL),
+    (dict(H=96), moe.MOE_EINVAL),
+    (dict(E=0), moe.MOE_EINVAL),
+    (dict(E=1024), moe.MOE_EINVAL),
+    (dict(top_k=0), moe.MOE_EINVAL),
+    (dict(top_k=17, E=64), moe.MOE_EINVAL),
+    (dict(top_k=9, E=8), moe.MOE_EINVAL),
+    (dict(I=100), moe.MOE_EINVAL),
+    (dict(I_shared=-64), moe.MOE_EINVAL),
+    (dict(I_shared=100), moe.MOE_EINVAL),
+    (dict(chunk_T=-1), moe.MOE_EINVAL),
+    (dict(act="f32", w="bf16"), moe.MOE_EUNSUPPORTED),
+    (dict(act="f32", w="mxfp4"), moe.MOE_EUNSUPPORTED),
+    (dict(w="mxfp4", H=2112), moe.MOE_EINVAL),
+    (dict(w="mxfp4", I_shared=128), moe.MOE_EUNSUPPORTED),
+])
+def test_shape_errors(bad, code):
+    assert call(shape(**bad)) == code
+    assert moe.moe_last_error() != ""
+
+
+def test_null_and_alignment_errors():
+    assert moe.load().moe_forward(None, None, None, None, None, None, None, 0, None) == moe.MOE_EINVAL
+    sh = shape()
+    assert call(sh, w=FakeW(router_w=0)) == moe.MOE_EINVAL
+    assert call(sh, w=FakeW(w_up=0x7F0000000008)) == moe.MOE_EINVAL
+    assert call(sh, w=FakeW(router_bias=0x7F0000000002)) == moe.MOE_EINVAL
+    assert call(sh, x=0) == moe.MOE_EINVAL
+    assert call(sh, y=0x7F2000000004) == moe.MOE_EINVAL
+    assert call(sh, idx=0) == moe.MOE_EINVAL
+    assert call(sh, tw=0x7F5000000001) == moe.MOE_EINVAL
+    assert call(sh, ws=0) == moe.MOE_EINVAL
+    assert call(sh, ws=0x7F4000000010, ws_bytes=1 << 40) == moe.MOE_EINVAL  # not 256-aligned
+    # MXFP4 without scales, shared expert without weights
+    assert call(shape(w="mxfp4")) == moe.MOE_EINVAL
+    assert call(shape(I_shared=768)) == moe.MOE_EINVAL
+
+
+def test_workspace_too_small():
+    sh = shape()
+    need = moe.moe_workspace_bytes(sh)
+    assert call(sh, ws_bytes=need - 1) == moe.MOE_EWORKSPACE
+    assert "workspace" in moe.moe_last_error()
+
+
+def test_route_rejects_chunking():
+    lib = moe.load()
+    sh = shape(chunk_T=32)
+    w = FakeW()
+    rc = lib.moe_route(ctypes.byref(sh), ctypes.byref(w.c), 0x7F1000000000, 0x7F3000000000,
+                       None, None, None, None, 0x7F4000000000, 1 << 40, None)
+    assert rc == moe.MOE_EINVAL
+
+
+def test_zero_tokens_returns_ok_without_touching_buffers():
+    assert call(shape(T=0), x=0, y=0, idx=0, ws=0) == moe.MOE_OK
