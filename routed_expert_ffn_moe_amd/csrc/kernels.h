@@ -69,6 +69,11 @@ void launch_down(const ExpertArgs &a, hipStream_t st);
 int gemm_bm_gu(const ExpertArgs &a);  // row-block sizes of the tile lists
 int gemm_bm_dc(const ExpertArgs &a);
 
+// Weight-streaming bf16 kernels (expert_stream.hip), used when the shapes fit.
+bool stream_ok(const ExpertArgs &a, bool gu);
+int stream_bm(const ExpertArgs &a);
+void launch_stream(const ExpertArgs &a, bool gu, hipStream_t st);
+
 // MXFP4 expert weights (bf16 activations, no shared expert).
 int mxfp4_bm();
 void launch_gate_up_mxfp4(const ExpertArgs &a, hipStream_t st);
