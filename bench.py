@@ -175,6 +175,9 @@ def main():
                     help="comma-separated secondary workloads ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES (calibrates HBM "
+                         "byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this layer has no multi-GPU path here "
@@ -182,6 +185,14 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_probe:
+        src = torch.empty(args.copy_probe, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe, "copies": args.steps}))
+        return
     import routed_expert_ffn_moe_amd as moe
     moe.load()
     torch.cuda.set_device(0)

@@ -13,12 +13,13 @@
 //    weight element read once per tile.
 //  * The tile's token rows (gathered through row_src) are staged in LDS in
 //    double-buffered 128-wide K chunks shared by the 4 waves.
-//  * The MFMA takes the weights as its A operand and the tokens as B, so a
-//    lane ends up with 4 adjacent output columns of one token row and stores
-//    them as one 8-byte word.
-//  * Work items (weight tile, row tile) are dealt out XCD by XCD in weight-
-//    tile-major order, so the row tiles of one expert that share a weight
-//    tile run on the same XCD and hit its L2.
+//  * The MFMA takes the weights as its A operand and the tokens as B; with
+//    the weight rows of the two column blocks interleaved by fours, a lane
+//    ends up with 8 adjacent output columns of one token row and stores them
+//    as one 16-byte word (64 contiguous bytes per row and wave).
+//  * Work items are ordered expert-major (then weight tile, then row tile)
+//    and dealt out XCD by XCD in contiguous runs, so an expert's weight tiles
+//    and token rows are fetched into one XCD's L2 and reused there.
 #include "common.h"
 #include "kernels.h"
 
@@ -39,6 +40,7 @@ struct StreamP {
     uint16_t *out;            // GU: h; DC: stage
     const Tile *tiles;
     const int32_t *ntiles;
+    const uint32_t *items;
     int T, H, E, k, I, Is, ldh, ntn;
 };
 
@@ -75,12 +77,15 @@ __global__ __launch_bounds__(256) void expert_stream(StreamP p)
     constexpr int CB = 2;                      // 16-row weight blocks per wave
     constexpr int MB = BM / 16;                // 16-row token blocks
     constexpr int ACH = BM * (SKC / 8) / 256;  // 16-byte token chunks per thread
-    constexpr int SD = BM <= 16 ? 8 : 4;       // prefetch ring depth in 32-wide K steps
+    constexpr int SD = 8;                      // prefetch ring depth in 32-wide K steps
     static_assert(ACH >= 1 && ACH * 256 == BM * SKC / 8, "token staging");
+    static_assert(CB == 2, "the epilogue packs two column blocks per lane");
 
     __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * SLD];
 
-    // Work item: XCD-major deal of (weight tile, row tile), weight tile outer.
+    // Work item: the item list (expert-major, column tile, row tile) is
+    // dealt out in 8 contiguous runs, one per XCD (workgroups go round-robin
+    // over the XCDs), so one expert's tiles share an L2.
     const int ntiles = *p.ntiles;
     const int total = ntiles * p.ntn;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -88,8 +93,9 @@ __global__ __launch_bounds__(256) void expert_stream(StreamP p)
     const int wi = xcd * per + slot;
     if (slot >= per || wi >= total)
         return;
-    const int nt = wi / ntiles;
-    const Tile tile = p.tiles[wi - nt * ntiles];
+    const uint32_t item = p.items[wi];
+    const int nt = (int)(item >> 20);
+    const Tile tile = p.tiles[item & 0xFFFFF];
     const int g = tile.g, row0 = tile.row0;
     const bool routed = g < p.E;
     const int nrows = min(BM, p.offsets[g + 1] - row0);
@@ -104,7 +110,10 @@ __global__ __launch_bounds__(256) void expert_stream(StreamP p)
     const int l16 = lane & 15, lg = lane >> 4;
     const int mbn = (nrows + 15) >> 4;  // row blocks holding tokens (uniform)
 
-    // Weight rows of this lane: matrix m, block cb -> row n0 + wave*32 + cb*16 + l16.
+    // Weight rows of this lane: MFMA row l16 of block cb is weight row
+    // n0 + wave*32 + 8*(l16/4) + 4*cb + l16%4, so that after the MFMA the lane
+    // with lg = l16/4 holds 8 consecutive output columns (4 per block) and
+    // stores them as one 16-byte word.
     const int64_t wstride = (int64_t)N * K;
     const uint16_t *wbase0 = routed ? p.w0 + (int64_t)g * wstride : p.s0;
     const uint16_t *wbase1 = GU ? (routed ? p.w1 + (int64_t)g * wstride : p.s1) : nullptr;
@@ -114,7 +123,8 @@ __global__ __launch_bounds__(256) void expert_stream(StreamP p)
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
             wp[m][cb] = (m == 0 ? wbase0 : wbase1) +
-                        (int64_t)(n0 + wave * 32 + cb * 16 + l16) * K + lg * 8;
+                        (int64_t)(n0 + wave * 32 + 8 * (l16 >> 2) + 4 * cb + (l16 & 3)) * K +
+                        lg * 8;
 
     // Token rows staged by this thread: all row_src loads first, then the
     // row pointers (selects, no branches).
@@ -203,35 +213,33 @@ __global__ __launch_bounds__(256) void expert_stream(StreamP p)
         }
     }
 
-    // Epilogue: lane holds columns n .. n+3 of token row mb*16 + l16.
+    // Epilogue: lane holds columns n .. n+7 of token row mb*16 + l16
+    // (block cb covers n + 4*cb .. n + 4*cb + 3).
+    const int n = n0 + wave * 32 + lg * 8;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         const int mr = mb * 16 + l16;
         if (mr >= nrows)
             continue;
         const int pos = row0 + mr;
+        uint4 o;
         if (GU) {
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-                const int n = n0 + wave * 32 + cb * 16 + lg * 4;
-                const floatx4 gv = acc[0][cb][mb], uv = acc[NB - 1][cb][mb];
-                uint2 o;
-                o.x = pack_bf2(silu(gv[0]) * uv[0], silu(gv[1]) * uv[1]);
-                o.y = pack_bf2(silu(gv[2]) * uv[2], silu(gv[3]) * uv[3]);
-                *(uint2 *)(p.out + (int64_t)pos * p.ldh + n) = o;
-            }
+            const floatx4 g0 = acc[0][0][mb], u0 = acc[NB - 1][0][mb];
+            const floatx4 g1 = acc[0][1][mb], u1 = acc[NB - 1][1][mb];
+            o.x = pack_bf2(silu(g0[0]) * u0[0], silu(g0[1]) * u0[1]);
+            o.y = pack_bf2(silu(g0[2]) * u0[2], silu(g0[3]) * u0[3]);
+            o.z = pack_bf2(silu(g1[0]) * u1[0], silu(g1[1]) * u1[1]);
+            o.w = pack_bf2(silu(g1[2]) * u1[2], silu(g1[3]) * u1[3]);
+            *(uint4 *)(p.out + (int64_t)pos * p.ldh + n) = o;
         } else {
             const int pr = p.row_src[pos];
             const float wt = pr < n_pairs ? p.topk_w[pr] : 1.0f;
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-                const int n = n0 + wave * 32 + cb * 16 + lg * 4;
-                const floatx4 v = acc[0][cb][mb];
-                uint2 o;
-                o.x = pack_bf2(v[0] * wt, v[1] * wt);
-                o.y = pack_bf2(v[2] * wt, v[3] * wt);
-                *(uint2 *)(p.out + (int64_t)pr * p.H + n) = o;
-            }
+            const floatx4 v0 = acc[0][0][mb], v1 = acc[0][1][mb];
+            o.x = pack_bf2(v0[0] * wt, v0[1] * wt);
+            o.y = pack_bf2(v0[2] * wt, v0[3] * wt);
+            o.z = pack_bf2(v1[0] * wt, v1[1] * wt);
+            o.w = pack_bf2(v1[2] * wt, v1[3] * wt);
+            *(uint4 *)(p.out + (int64_t)pr * p.H + n) = o;
         }
     }
 }
@@ -251,6 +259,7 @@ void run(const ExpertArgs &a, hipStream_t st)
     p.out = (uint16_t *)(GU ? a.h : a.stage);
     p.tiles = GU ? a.tiles_gu : a.tiles_dc;
     p.ntiles = GU ? a.ntiles_gu : a.ntiles_dc;
+    p.items = GU ? a.items_gu : a.items_dc;
     p.T = a.T;
     p.H = a.H;
     p.E = a.E;
@@ -276,6 +285,14 @@ bool stream_ok(const ExpertArgs &a, bool gu)
     if (gu)
         return a.H % 256 == 0 && a.I % WROWS == 0 && a.I_shared % WROWS == 0;
     return a.I % 256 == 0 && a.I_shared % 256 == 0 && a.H % WROWS == 0;
+}
+
+int stream_ntn(const ExpertArgs &a, bool gu)
+{
+    if (!stream_ok(a, gu))
+        return 0;
+    const int N = gu ? (a.I > a.I_shared ? a.I : a.I_shared) : a.H;
+    return (N + WROWS - 1) / WROWS;
 }
 
 int stream_bm(const ExpertArgs &a)

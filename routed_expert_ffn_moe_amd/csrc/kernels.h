@@ -38,6 +38,10 @@ struct PermuteArgs {
     Tile *tiles_b;        // tile list for row-block size bm_b
     int32_t *ntiles_b;
     int bm_a, bm_b;
+    // Optional work-item lists (expert-major, then column tile, then row
+    // tile): item = tile index | column tile << 20, ntn_* column tiles each.
+    uint32_t *items_a, *items_b;
+    int ntn_a, ntn_b;
     int T, E, k, shared;
 };
 int permute_blocks(int n_pairs);  // number of histogram blocks
@@ -60,6 +64,7 @@ struct ExpertArgs {
     const int32_t *ntiles_gu;
     const Tile *tiles_dc;
     const int32_t *ntiles_dc;
+    const uint32_t *items_gu, *items_dc;   // work items of the streaming kernels
     int max_tiles_gu, max_tiles_dc;
     int T, H, E, k, I, I_shared, act, wdt;
     int shape_T;  // tokens of a full pass: selects the tile shape
@@ -72,6 +77,7 @@ int gemm_bm_dc(const ExpertArgs &a);
 // Weight-streaming bf16 kernels (expert_stream.hip), used when the shapes fit.
 bool stream_ok(const ExpertArgs &a, bool gu);
 int stream_bm(const ExpertArgs &a);
+int stream_ntn(const ExpertArgs &a, bool gu);  // column tiles (0 if not streaming)
 void launch_stream(const ExpertArgs &a, bool gu, hipStream_t st);
 
 // MXFP4 expert weights (bf16 activations, no shared expert).

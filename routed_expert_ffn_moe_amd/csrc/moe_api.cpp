@@ -112,8 +112,9 @@ int check_weights(const moe_shape_t *s, const moe_weights_t *w)
 
 // Workspace layout of one pass of Tc tokens.
 struct Layout {
-    size_t logits, wts, blk, counts, offsets, row_src, tiles_gu, ntiles, tiles_dc, h, stage, total;
-    int max_tiles_gu, max_tiles_dc, bm_gu, bm_dc;
+    size_t logits, wts, blk, counts, offsets, row_src, tiles_gu, ntiles, tiles_dc, items_gu,
+        items_dc, h, stage, total;
+    int max_tiles_gu, max_tiles_dc, bm_gu, bm_dc, ntn_gu, ntn_dc;
 };
 
 moe::ExpertArgs expert_shape(const moe_shape_t *s, int Tc)
@@ -148,6 +149,8 @@ Layout layout(const moe_shape_t *s, int Tc)
     L.bm_dc = moe::gemm_bm_dc(a);
     L.max_tiles_gu = max_tiles(Tc, s, L.bm_gu);
     L.max_tiles_dc = max_tiles(Tc, s, L.bm_dc);
+    L.ntn_gu = moe::stream_ntn(a, true);
+    L.ntn_dc = moe::stream_ntn(a, false);
     const int64_t pairs = (int64_t)Tc * s->top_k;
     const int64_t rows = pairs + (s->I_shared > 0 ? Tc : 0);
     const int64_t ldh = std::max(s->I, s->I_shared);
@@ -167,6 +170,8 @@ Layout layout(const moe_shape_t *s, int Tc)
     L.tiles_gu = take((size_t)L.max_tiles_gu * sizeof(moe::Tile));
     L.ntiles = take(2 * 4);
     L.tiles_dc = take((size_t)L.max_tiles_dc * sizeof(moe::Tile));
+    L.items_gu = take((size_t)L.max_tiles_gu * L.ntn_gu * 4);
+    L.items_dc = take((size_t)L.max_tiles_dc * L.ntn_dc * 4);
     L.h = take((size_t)rows * ldh * esz);
     L.stage = take((size_t)rows * s->H * esz);
     L.total = off;
@@ -272,6 +277,10 @@ int route_pass(const moe_shape_t *s, const moe_weights_t *w, const void *x, int 
     p.ntiles_b = (int32_t *)(ws + L.ntiles) + 1;
     p.bm_a = L.bm_gu;
     p.bm_b = L.bm_dc;
+    p.items_a = L.ntn_gu ? (uint32_t *)(ws + L.items_gu) : nullptr;
+    p.items_b = L.ntn_dc ? (uint32_t *)(ws + L.items_dc) : nullptr;
+    p.ntn_a = L.ntn_gu;
+    p.ntn_b = L.ntn_dc;
     p.T = Tc;
     p.E = s->E;
     p.k = s->top_k;
@@ -361,6 +370,8 @@ int moe_forward(const moe_shape_t *s, const moe_weights_t *w, const void *x, voi
         a.tiles_gu = (const moe::Tile *)(wsb + Lw.tiles_gu);
         a.ntiles_gu = (const int32_t *)(wsb + Lw.ntiles);
         a.tiles_dc = (const moe::Tile *)(wsb + Lw.tiles_dc);
+        a.items_gu = (const uint32_t *)(wsb + Lw.items_gu);
+        a.items_dc = (const uint32_t *)(wsb + Lw.items_dc);
         a.ntiles_dc = (const int32_t *)(wsb + Lw.ntiles) + 1;
         a.max_tiles_gu = Lw.max_tiles_gu;
         a.max_tiles_dc = Lw.max_tiles_dc;

@@ -52,7 +52,8 @@ __global__ __launch_bounds__(1024) void permute_scan(
     int32_t *__restrict__ blk, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     Tile *__restrict__ tiles_a, int32_t *__restrict__ ntiles_a, Tile *__restrict__ tiles_b,
     int32_t *__restrict__ ntiles_b, int bm_a, int bm_b, int nblk, int E, int n_pairs, int T,
-    int shared)
+    int shared, uint32_t *__restrict__ items_a, int ntn_a, uint32_t *__restrict__ items_b,
+    int ntn_b)
 {
     __shared__ int32_t s_cnt[1025];
     __shared__ int32_t s_ta[1025];
@@ -123,7 +124,8 @@ __global__ __launch_bounds__(1024) void permute_scan(
         for (int b = 0; b < nblk; ++b)
             blk[(int64_t)b * E + e] += o;
     }
-    // Tile lists.
+    // Tile lists, and the work items of each list: the tiles of expert g
+    // start at s_g; its items start at ntn * s_g, column tile outer.
     for (int g = tid; g < G; g += 1024) {
         int cg = g < E ? s_cnt[g] : T;
         int og = s_off[g];
@@ -131,6 +133,15 @@ __global__ __launch_bounds__(1024) void permute_scan(
             tiles_a[t] = Tile{g, og + r};
         for (int r = 0, t = s_tb[g]; r < cg; r += bm_b, ++t)
             tiles_b[t] = Tile{g, og + r};
+        const int na = (cg + bm_a - 1) / bm_a, nb = (cg + bm_b - 1) / bm_b;
+        if (items_a)
+            for (int nt = 0; nt < ntn_a; ++nt)
+                for (int m = 0; m < na; ++m)
+                    items_a[ntn_a * s_ta[g] + nt * na + m] = (uint32_t)(s_ta[g] + m) | ((uint32_t)nt << 20);
+        if (items_b)
+            for (int nt = 0; nt < ntn_b; ++nt)
+                for (int m = 0; m < nb; ++m)
+                    items_b[ntn_b * s_tb[g] + nt * nb + m] = (uint32_t)(s_tb[g] + m) | ((uint32_t)nt << 20);
     }
 }
 
@@ -185,7 +196,8 @@ void launch_permute(const PermuteArgs &a, hipStream_t st)
     if (nblk > 0)
         permute_hist<<<nblk, 256, a.E * sizeof(int32_t), st>>>(a.idx, a.blk, n_pairs, a.E);
     permute_scan<<<1, 1024, 0, st>>>(a.blk, a.counts, a.offsets, a.tiles_a, a.ntiles_a, a.tiles_b,
-                                     a.ntiles_b, a.bm_a, a.bm_b, nblk, a.E, n_pairs, a.T, a.shared);
+                                     a.ntiles_b, a.bm_a, a.bm_b, nblk, a.E, n_pairs, a.T, a.shared,
+                                     a.items_a, a.ntn_a, a.items_b, a.ntn_b);
     if (nblk > 0)
         permute_scatter<<<nblk, 64, a.E * sizeof(int32_t), st>>>(a.idx, a.blk, a.row_src, n_pairs,
                                                                  a.E, a.T, a.shared);
