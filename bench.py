@@ -223,6 +223,7 @@ def main():
                    "max_rows_per_expert": int(counts.max())},
         "roofline": roofline(work, dom, stages[dom], c["w"]),
         "stages_us": {k: round(v * 1e3, 2) for k, v in stages.items()},
+        "tuning": {k: v for k, v in os.environ.items() if k.startswith("MOE_")},
     }
     also = {}
     del wl

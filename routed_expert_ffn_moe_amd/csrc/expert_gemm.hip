@@ -7,10 +7,11 @@
 //           sections: SwiGLU(gate, up), gate is the SiLU branch; "DeepSeek
 //           V4.1F Q4 with native DSpark MTP", decode paragraph: fused
 //           gate+up+SwiGLU and bf16 rounding inside the producing kernel).
-//  down:    O = h Wd^T, each row scaled by its routing weight and rounded once
-//           into its own staging row (t*k + j), so no two pairs ever share an
-//           output location (same Jetson page, nondeterminism section).
-//  combine: y_t = sum_j stage[t*k + j] (+ shared row) in fixed j order.
+//  down:    O = h Wd^T, rounded once into the grouped row's own staging row,
+//           so no two pairs ever share an output location (same Jetson page,
+//           nondeterminism section).
+//  combine: y_t = sum_j w_tj * stage[row of (t, j)] (+ shared row) in fixed j
+//           order: the routing-weight scale and the deterministic sum.
 //
 // A workgroup owns one tile of the permutation's tile list (one expert, up to
 // BM consecutive grouped rows) and BN output columns.  X rows are gathered
@@ -184,12 +185,10 @@ __global__ __launch_bounds__(256) void expert_gemm_bf16(GemmP p)
                     p.out[(int64_t)pos * p.ldh + n] = f2bf(hv);
                 }
             } else {
-                const int pr = p.row_src[pos];
-                const float wt = pr < n_pairs ? p.topk_w[pr] : 1.0f;
 #pragma unroll
                 for (int b = 0; b < NBL; ++b) {
                     const int n = n0 + wave * WNC + b * 16 + fr;
-                    p.out[(int64_t)pr * p.H + n] = f2bf(acc[0][a][b][i] * wt);
+                    p.out[(int64_t)pos * p.H + n] = f2bf(acc[0][a][b][i]);
                 }
             }
         }
@@ -243,17 +242,18 @@ __global__ __launch_bounds__(256) void expert_gemm_f32(GemmF32 p)
         float s = 0.0f;
         for (int kk = 0; kk < K; ++kk)
             s = fmaf(a[kk], wd[kk], s);
-        const int pr = p.row_src[pos];
-        const float wt = pr < n_pairs ? p.topk_w[pr] : 1.0f;
-        p.out[(int64_t)pr * p.H + n] = s * wt;
+        p.out[(int64_t)pos * p.H + n] = s;
     }
 }
 
 // ---- combine ---------------------------------------------------------------
 
-// y[t, c] = sum_j stage[t*k + j, c] (+ stage[T*k + t, c]), fp32 sum in j
-// order, rounded once.  Each thread handles 8 consecutive columns.
+// y[t, c] = sum_j w[t*k + j] * stage[row_of[t*k + j], c] (+ stage[T*k + t, c]),
+// fp32 sum in j order, rounded once.  Each thread handles 8 consecutive
+// columns; the staging rows are gathered whole.
 __global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__ stage,
+                                                    const int32_t *__restrict__ row_of,
+                                                    const float *__restrict__ topk_w,
                                                     uint16_t *__restrict__ y, int T, int H, int k,
                                                     int shared)
 {
@@ -265,13 +265,21 @@ __global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const int n_rows = k + (shared ? 1 : 0);
     for (int j = 0; j < n_rows; ++j) {
-        const int64_t row = j < k ? (int64_t)t * k + j : (int64_t)T * k + t;
+        int64_t row;
+        float w;
+        if (j < k) {
+            row = row_of[(int64_t)t * k + j];
+            w = topk_w[(int64_t)t * k + j];
+        } else {
+            row = (int64_t)T * k + t;
+            w = 1.0f;
+        }
         const uint4 v = *(const uint4 *)(stage + row * H + c8);
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            acc[2 * q] += bf2f((uint16_t)(w4[q] & 0xFFFF));
-            acc[2 * q + 1] += bf2f((uint16_t)(w4[q] >> 16));
+            acc[2 * q] = fmaf(w, bf2f((uint16_t)(w4[q] & 0xFFFF)), acc[2 * q]);
+            acc[2 * q + 1] = fmaf(w, bf2f((uint16_t)(w4[q] >> 16)), acc[2 * q + 1]);
         }
     }
     uint4 o;
@@ -283,6 +291,8 @@ __global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__
 }
 
 __global__ __launch_bounds__(256) void combine_f32(const float *__restrict__ stage,
+                                                   const int32_t *__restrict__ row_of,
+                                                   const float *__restrict__ topk_w,
                                                    float *__restrict__ y, int T, int H, int k,
                                                    int shared)
 {
@@ -291,8 +301,10 @@ __global__ __launch_bounds__(256) void combine_f32(const float *__restrict__ sta
         return;
     const int t = (int)(i / H), c = (int)(i % H);
     float acc = 0.0f;
-    for (int j = 0; j < k; ++j)
-        acc += stage[((int64_t)t * k + j) * H + c];
+    for (int j = 0; j < k; ++j) {
+        const int64_t q = (int64_t)t * k + j;
+        acc = fmaf(topk_w[q], stage[(int64_t)row_of[q] * H + c], acc);
+    }
     if (shared)
         acc += stage[((int64_t)T * k + t) * H + c];
     y[i] = acc;
@@ -431,11 +443,11 @@ void launch_combine(const CombineArgs &a, hipStream_t st)
     if (a.act == ACT_BF16) {
         const int64_t n = (int64_t)a.T * (a.H / 8);
         combine_bf16<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
-            (const uint16_t *)a.stage, (uint16_t *)a.y, a.T, a.H, a.k, a.shared);
+            (const uint16_t *)a.stage, a.row_of, a.topk_w, (uint16_t *)a.y, a.T, a.H, a.k, a.shared);
     } else {
         const int64_t n = (int64_t)a.T * a.H;
         combine_f32<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
-            (const float *)a.stage, (float *)a.y, a.T, a.H, a.k, a.shared);
+            (const float *)a.stage, a.row_of, a.topk_w, (float *)a.y, a.T, a.H, a.k, a.shared);
     }
 }
 

@@ -23,13 +23,18 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+#include <cstdlib>
+
 namespace moe {
 
 namespace {
 
 constexpr int SKC = 128;      // K elements of one staged token chunk
 constexpr int SLD = SKC + 8;  // padded LDS row (bf16), 272 bytes
-constexpr int WROWS = 128;    // weight rows per workgroup and matrix (4 waves x 32)
+// Weight rows per work item and matrix: 4 waves x 32 (gate+up, two
+// matrices) or 4 waves x 64 (down, one matrix).
+constexpr int wrows_of(bool gu) { return gu ? 128 : 256; }
 
 struct StreamP {
     const uint16_t *x;        // GU: activations [T, H]; DC: h [rows, ldh]
@@ -40,7 +45,8 @@ struct StreamP {
     uint16_t *out;            // GU: h; DC: stage
     const Tile *tiles;
     const int32_t *ntiles;
-    const uint32_t *items;
+    const int4 *items;
+    const int32_t *row_tok;
     int T, H, E, k, I, Is, ldh, ntn;
 };
 
@@ -50,19 +56,6 @@ template <int N>
 using u32v = uint32_t __attribute__((ext_vector_type(4 * N)));
 
 template <int N>
-__device__ __forceinline__ void chunk_load(u32v<N> &r, const uint16_t *const (&src)[N], int off)
-{
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const uint4 t = *(const uint4 *)(src[i] + off);
-        r[4 * i] = t.x;
-        r[4 * i + 1] = t.y;
-        r[4 * i + 2] = t.z;
-        r[4 * i + 3] = t.w;
-    }
-}
-
-template <int N>
 __device__ __forceinline__ void chunk_store(const u32v<N> &r, uint16_t *dst, const int (&off)[N])
 {
 #pragma unroll
@@ -70,181 +63,271 @@ __device__ __forceinline__ void chunk_store(const u32v<N> &r, uint16_t *dst, con
         *(uint4 *)(dst + off[i]) = uint4{r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]};
 }
 
-template <int BM, bool GU>
-__global__ __launch_bounds__(256) void expert_stream(StreamP p)
+// One work item: up to BM rows of one expert (group g) and a 128-row slice
+// of its weight matrices starting at weight row n0.  Uniform across the
+// workgroup; read as one 16-byte record.
+struct Item {
+    int g, row0, nrows, n0;
+};
+
+__device__ __forceinline__ Item item_at(const int4 *__restrict__ items, int wi)
 {
-    constexpr int NB = GU ? 2 : 1;             // weight matrices
-    constexpr int CB = 2;                      // 16-row weight blocks per wave
-    constexpr int MB = BM / 16;                // 16-row token blocks
-    constexpr int ACH = BM * (SKC / 8) / 256;  // 16-byte token chunks per thread
-    constexpr int SD = 8;                      // prefetch ring depth in 32-wide K steps
-    static_assert(ACH >= 1 && ACH * 256 == BM * SKC / 8, "token staging");
-    static_assert(CB == 2, "the epilogue packs two column blocks per lane");
+    // A uniform index into read-only memory: a scalar load, waited for on
+    // its own counter, so fetching records never drains the weight stream;
+    // and every branch and select on the record stays uniform.
+    const int4 r = items[__builtin_amdgcn_readfirstlane(wi)];
+    return Item{__builtin_amdgcn_readfirstlane(r.x), __builtin_amdgcn_readfirstlane(r.y),
+                __builtin_amdgcn_readfirstlane(r.z), __builtin_amdgcn_readfirstlane(r.w)};
+}
 
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * SLD];
+// Element offsets (into x or h) of the token rows this thread stages.
+template <int ACH, bool GU>
+__device__ __forceinline__ void item_rows(const StreamP &p, const Item &it, int tid, int (&aro)[ACH])
+{
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+        const int pos = it.row0 + min((tid + 256 * i) >> 4, it.nrows - 1);
+        aro[i] = GU ? p.row_tok[pos] * p.H : pos * p.ldh;
+    }
+}
 
-    // Work item: the item list (expert-major, column tile, row tile) is
-    // dealt out in 8 contiguous runs, one per XCD (workgroups go round-robin
-    // over the XCDs), so one expert's tiles share an L2.
-    const int ntiles = *p.ntiles;
-    const int total = ntiles * p.ntn;
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int per = (total + 7) >> 3;
-    const int wi = xcd * per + slot;
-    if (slot >= per || wi >= total)
-        return;
-    const uint32_t item = p.items[wi];
-    const int nt = (int)(item >> 20);
-    const Tile tile = p.tiles[item & 0xFFFFF];
-    const int g = tile.g, row0 = tile.row0;
-    const bool routed = g < p.E;
-    const int nrows = min(BM, p.offsets[g + 1] - row0);
-    const int n_pairs = p.T * p.k;
-    const int N = GU ? (routed ? p.I : p.Is) : p.H;
-    const int K = GU ? p.H : (routed ? p.I : p.Is);
-    const int n0 = nt * WROWS;
-    if (n0 >= N)
-        return;
+template <int ACH>
+__device__ __forceinline__ void rows_load(u32v<ACH> &r, const uint16_t *x, const int (&aro)[ACH],
+                                          int off)
+{
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+        const uint4 t = *(const uint4 *)(x + aro[i] + off);
+        r[4 * i] = t.x;
+        r[4 * i + 1] = t.y;
+        r[4 * i + 2] = t.z;
+        r[4 * i + 3] = t.w;
+    }
+}
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l16 = lane & 15, lg = lane >> 4;
-    const int mbn = (nrows + 15) >> 4;  // row blocks holding tokens (uniform)
-
-    // Weight rows of this lane: MFMA row l16 of block cb is weight row
-    // n0 + wave*32 + 8*(l16/4) + 4*cb + l16%4, so that after the MFMA the lane
-    // with lg = l16/4 holds 8 consecutive output columns (4 per block) and
-    // stores them as one 16-byte word.
-    const int64_t wstride = (int64_t)N * K;
-    const uint16_t *wbase0 = routed ? p.w0 + (int64_t)g * wstride : p.s0;
-    const uint16_t *wbase1 = GU ? (routed ? p.w1 + (int64_t)g * wstride : p.s1) : nullptr;
-    const uint16_t *wp[NB][CB];
+// One 32-wide K step (step s4 of a token chunk) over the first NMB token
+// blocks: consume the weight fragments of ring slot `slot` and refill it from
+// wl + wk (the step SD steps ahead), then run the token blocks.
+template <int NMB, int MB, int NB, int CB, int SD>
+__device__ __forceinline__ void kstep(const uint16_t *As, int slot, int s4, int l16, int lg,
+                                      uint4 (&bq)[SD][NB][CB], const uint16_t *const (&wl)[NB],
+                                      int wk, const int (&woff)[CB], floatx4 (&acc)[NB][CB][MB])
+{
+    // Take the weight fragments of this step and refill their ring slot.
+    bf16x8 wf[NB][CB];
 #pragma unroll
     for (int m = 0; m < NB; ++m)
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-            wp[m][cb] = (m == 0 ? wbase0 : wbase1) +
-                        (int64_t)(n0 + wave * 32 + 8 * (l16 >> 2) + 4 * cb + (l16 & 3)) * K +
-                        lg * 8;
-
-    // Token rows staged by this thread: all row_src loads first, then the
-    // row pointers (selects, no branches).
-    const uint16_t *asrc[ACH];
-    int aoff[ACH];
-    int prow[ACH];
+        for (int cb = 0; cb < CB; ++cb) {
+            wf[m][cb] = as_bf16x8(bq[slot][m][cb]);
+            bq[slot][m][cb] = *(const uint4 *)(wl[m] + woff[cb] + wk);
+        }
+    // issue the refills here, not later: the wait for this step's token
+    // chunk must not have to wait for them
+    __builtin_amdgcn_sched_barrier(0);
+    // Token block by token block: each LDS fragment feeds NB*CB MFMAs, so
+    // the next block's read overlaps the current block's MFMAs.
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-        const int r = (tid + 256 * i) >> 4;
-        prow[i] = GU ? p.row_src[row0 + min(r, nrows - 1)] : row0 + min(r, nrows - 1);
+    for (int mb = 0; mb < NMB; ++mb) {
+        const bf16x8 tf =
+            as_bf16x8(*(const uint4 *)(As + (mb * 16 + l16) * SLD + s4 * 32 + lg * 8));
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+                acc[m][cb][mb] = mfma16(wf[m][cb], tf, acc[m][cb][mb]);
     }
-    const int nsteps = K / 32;
-    const int nchunks = K / SKC;  // even: K % 256 == 0
+}
 
-    // Weight prefetch goes out before the row pointers are needed.
+// Persistent: the workgroup walks its run of work items; the weight prefetch
+// ring and the token-chunk pipeline run on across item boundaries, so the
+// next item's first weights and rows are in flight while the current one
+// finishes.  Item records are fetched two items ahead and row tokens one item
+// ahead, so no wait on them ever drains the weight stream.  All items of a
+// launch share N and K (the shared expert, if any, has the routed width).
+template <int BM, bool GU, int SD>
+__global__ __launch_bounds__(256) void expert_stream(StreamP p, const int4 *__restrict__ items)
+{
+    constexpr int NB = GU ? 2 : 1;             // weight matrices
+    constexpr int CB = GU ? 2 : 4;             // 16-row weight blocks per wave and matrix
+    constexpr int MB = BM / 16;                // 16-row token blocks
+    constexpr int ACH = BM * (SKC / 8) / 256;  // 16-byte token chunks per thread
+    static_assert(SD == 2 || SD == 4 || SD == 8, "prefetch ring depth in K steps");
+    static_assert(ACH >= 1 && ACH * 256 == BM * SKC / 8, "token staging");
+    static_assert(CB % 2 == 0 && 4 * CB * 16 == wrows_of(GU), "column blocks go in pairs");
+
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * SLD];
+
+    const int ntiles = *p.ntiles;
+    const int total = ntiles * p.ntn;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
+    const int per = (total + 7) >> 3;
+    // The items of this workgroup: run position slot + j * nslot, j = 0, 1, ...
+    const int base = xcd * per;
+    const int lim = min(per, total - base);  // items in this XCD's run
+    if (slot >= lim)
+        return;
+    const int nitems = (lim - slot + nslot - 1) / nslot;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int n_pairs = p.T * p.k;
+    const int N = GU ? p.I : p.H;
+    const int K = GU ? p.H : p.I;
+    const int nchunks = K / SKC;  // even, >= 2
+    const int64_t wstride = (int64_t)N * K;
+
+    // Weight rows of this lane: the blocks go in pairs of 32 rows; MFMA row
+    // l16 of block cb is weight row n0 + wave*16*CB + 32*(cb/2) + 8*(l16/4) +
+    // 4*(cb%2) + l16%4, so that after the MFMA the lane with lg = l16/4 holds
+    // 8 consecutive output columns per pair and stores them as one 16-byte word.
+    int woff[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+        woff[cb] = (wave * 16 * CB + 32 * (cb >> 1) + 8 * (l16 >> 2) + 4 * (cb & 1) + (l16 & 3)) * K +
+                   lg * 8;
+    auto wbase = [&](const Item &it, int m) -> const uint16_t * {
+        const bool routed = it.g < p.E;
+        const uint16_t *W = m == 0 ? (routed ? p.w0 + (int64_t)it.g * wstride : p.s0)
+                                   : (routed ? p.w1 + (int64_t)it.g * wstride : p.s1);
+        return W + (int64_t)it.n0 * K;
+    };
+    int aoff[ACH];
+#pragma unroll
+    for (int i = 0; i < ACH; ++i)
+        aoff[i] = ((tid + 256 * i) >> 4) * SLD + (tid & 15) * 8;
+
+    // Prologue: first item's weights for chunk 0, its token rows, chunk 0 in LDS.
+    Item cur = item_at(items, base + slot);
+    Item nxt = item_at(items, base + slot + min(1, nitems - 1) * nslot);
+    const uint16_t *wc[NB];
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+        wc[m] = wbase(cur, m);
     uint4 bq[SD][NB][CB];
-    // Loads are never predicated (a branch around a load makes the compiler
-    // wait for every outstanding load): steps past the end re-read the last.
 #pragma unroll
     for (int d = 0; d < SD; ++d)
 #pragma unroll
         for (int m = 0; m < NB; ++m)
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb)
-                bq[d][m][cb] = *(const uint4 *)(wp[m][cb] + min(d, nsteps - 1) * 32);
-
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-        const int q = tid + 256 * i;
-        const int r = q >> 4, c8 = q & 15;
-        int64_t roff;
-        if (GU) {
-            const int pr = prow[i];
-            const int t = pr < n_pairs ? pr / p.k : pr - n_pairs;
-            roff = (int64_t)t * p.H;
-        } else {
-            roff = (int64_t)prow[i] * p.ldh;
-        }
-        asrc[i] = p.x + roff + c8 * 8;
-        aoff[i] = r * SLD + c8 * 8;
-    }
+                bq[d][m][cb] = *(const uint4 *)(wc[m] + woff[cb] + d * 32);  // SD <= 8 <= K/32
+    int aro[ACH], aro_n[ACH];
+    item_rows<ACH, GU>(p, cur, tid, aro);
+    item_rows<ACH, GU>(p, nxt, tid, aro_n);
     u32v<ACH> ra;
-
-    floatx4 acc[NB][CB][MB];
-#pragma unroll
-    for (int m = 0; m < NB; ++m)
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-                acc[m][cb][mb] = floatx4{0, 0, 0, 0};
-
-    chunk_load<ACH>(ra, asrc, 0);
+    rows_load<ACH>(ra, p.x, aro, (tid & 15) * 8);
     chunk_store<ACH>(ra, sA[0], aoff);
     __syncthreads();
-    chunk_load<ACH>(ra, asrc, min(1, nchunks - 1) * SKC);
+    rows_load<ACH>(ra, p.x, aro, SKC + (tid & 15) * 8);
+    int buf = 0;
 
-    for (int c = 0; c < nchunks; c += 2) {
+    for (int j = 0; j < nitems; ++j) {
+        // record of the item after next (clamped: re-read of the last one)
+        const Item nn = item_at(items, base + slot + min(j + 2, nitems - 1) * nslot);
+        // Next item's weights; the last item points them at itself, so the
+        // prefetches that run past it stay in bounds and no branch is needed.
+        const uint16_t *wn[NB];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int cc = c + h;
-            const uint16_t *As = sA[cc & 1];
+        for (int m = 0; m < NB; ++m)
+            wn[m] = j + 1 < nitems ? wbase(nxt, m) : wc[m];
+
+        floatx4 acc[NB][CB][MB];
 #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-                const int d = (h * 4 + s4) % SD;
-                const int step = cc * 4 + s4;
-                bf16x8 tf[MB];
+        for (int m = 0; m < NB; ++m)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
-                    tf[mb] = as_bf16x8(*(const uint4 *)(As + (mb * 16 + l16) * SLD + s4 * 32 + lg * 8));
-#pragma unroll
-                for (int m = 0; m < NB; ++m)
-#pragma unroll
-                    for (int cb = 0; cb < CB; ++cb) {
-                        const bf16x8 wf = as_bf16x8(bq[d][m][cb]);
-                        bq[d][m][cb] = *(const uint4 *)(wp[m][cb] + min(step + SD, nsteps - 1) * 32);
-#pragma unroll
-                        for (int mb = 0; mb < MB; ++mb)
-                            if (mb < mbn)  // row blocks past the tile's rows are skipped
-                                acc[m][cb][mb] = mfma16(wf, tf[mb], acc[m][cb][mb]);
-                    }
-            }
-            chunk_store<ACH>(ra, sA[(cc + 1) & 1], aoff);
-            __syncthreads();
-            chunk_load<ACH>(ra, asrc, min(cc + 2, nchunks - 1) * SKC);
-        }
-    }
+                    acc[m][cb][mb] = floatx4{0, 0, 0, 0};
 
-    // Epilogue: lane holds columns n .. n+7 of token row mb*16 + l16
-    // (block cb covers n + 4*cb .. n + 4*cb + 3).
-    const int n = n0 + wave * 32 + lg * 8;
+        for (int c = 0; c < nchunks; c += 2) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const int mr = mb * 16 + l16;
-        if (mr >= nrows)
-            continue;
-        const int pos = row0 + mr;
-        uint4 o;
-        if (GU) {
-            const floatx4 g0 = acc[0][0][mb], u0 = acc[NB - 1][0][mb];
-            const floatx4 g1 = acc[0][1][mb], u1 = acc[NB - 1][1][mb];
-            o.x = pack_bf2(silu(g0[0]) * u0[0], silu(g0[1]) * u0[1]);
-            o.y = pack_bf2(silu(g0[2]) * u0[2], silu(g0[3]) * u0[3]);
-            o.z = pack_bf2(silu(g1[0]) * u1[0], silu(g1[1]) * u1[1]);
-            o.w = pack_bf2(silu(g1[2]) * u1[2], silu(g1[3]) * u1[3]);
-            *(uint4 *)(p.out + (int64_t)pos * p.ldh + n) = o;
-        } else {
-            const int pr = p.row_src[pos];
-            const float wt = pr < n_pairs ? p.topk_w[pr] : 1.0f;
-            const floatx4 v0 = acc[0][0][mb], v1 = acc[0][1][mb];
-            o.x = pack_bf2(v0[0] * wt, v0[1] * wt);
-            o.y = pack_bf2(v0[2] * wt, v0[3] * wt);
-            o.z = pack_bf2(v1[0] * wt, v1[1] * wt);
-            o.w = pack_bf2(v1[2] * wt, v1[3] * wt);
-            *(uint4 *)(p.out + (int64_t)pr * p.H + n) = o;
+            for (int h = 0; h < 2; ++h) {
+                const int cc = c + h;
+                const uint16_t *As = sA[buf];
+                // Weight chunks d = 0, 1, 2 after this one, from this item or
+                // (past its end) from the next one; branch-free on purpose.
+                const uint16_t *wl[3][NB];
+#pragma unroll
+                for (int d = 0; d < 3; ++d) {
+                    const int t = cc + d;
+                    const int over = t >= nchunks;
+                    const int tk = (t - over * nchunks) * SKC;
+#pragma unroll
+                    for (int m = 0; m < NB; ++m)
+                        wl[d][m] = (over ? wn[m] : wc[m]) + tk;
+                }
+                // Every row block is computed, also those past the tile's rows:
+                // such tiles are bound by their weight stream, not by the MFMAs.
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4)
+                    kstep<MB, MB, NB, CB, SD>(As, (h * 4 + s4) % SD, s4, l16, lg, bq,
+                                              wl[(s4 + SD) / 4], ((s4 + SD) % 4) * 32, woff, acc);
+                // Token chunk pipeline: ra holds the chunk after this one.
+                chunk_store<ACH>(ra, sA[buf ^ 1], aoff);
+                __syncthreads();
+                buf ^= 1;
+                const int c2 = cc + 2;
+                const int over = c2 >= nchunks;
+                int rsel[ACH];
+#pragma unroll
+                for (int i = 0; i < ACH; ++i)
+                    rsel[i] = over ? aro_n[i] : aro[i];
+                rows_load<ACH>(ra, p.x, rsel, (c2 - over * nchunks) * SKC + (tid & 15) * 8);
+                // keep these loads ahead of the next steps' weight loads, so
+                // that waiting for them never waits for the weight stream
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
+
+        // Epilogue: for block pair q the lane holds columns n + 32q .. +7 of
+        // token row mb*16 + l16 (block 2q covers the first four).
+        const int n = cur.n0 + wave * 16 * CB + lg * 8;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int mr = mb * 16 + l16;
+            if (mr >= cur.nrows)
+                continue;
+            const int pos = cur.row0 + mr;
+            if (GU) {
+#pragma unroll
+                for (int q = 0; q < CB / 2; ++q) {
+                    const floatx4 g0 = acc[0][2 * q][mb], u0 = acc[NB - 1][2 * q][mb];
+                    const floatx4 g1 = acc[0][2 * q + 1][mb], u1 = acc[NB - 1][2 * q + 1][mb];
+                    uint4 o;
+                    o.x = pack_bf2(silu(g0[0]) * u0[0], silu(g0[1]) * u0[1]);
+                    o.y = pack_bf2(silu(g0[2]) * u0[2], silu(g0[3]) * u0[3]);
+                    o.z = pack_bf2(silu(g1[0]) * u1[0], silu(g1[1]) * u1[1]);
+                    o.w = pack_bf2(silu(g1[2]) * u1[2], silu(g1[3]) * u1[3]);
+                    *(uint4 *)(p.out + (int64_t)pos * p.ldh + n + 32 * q) = o;
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < CB / 2; ++q) {
+                    const floatx4 v0 = acc[0][2 * q][mb], v1 = acc[0][2 * q + 1][mb];
+                    uint4 o;
+                    o.x = pack_bf2(v0[0], v0[1]);
+                    o.y = pack_bf2(v0[2], v0[3]);
+                    o.z = pack_bf2(v1[0], v1[1]);
+                    o.w = pack_bf2(v1[2], v1[3]);
+                    *(uint4 *)(p.out + (int64_t)pos * p.H + n + 32 * q) = o;
+                }
+            }
+        }
+        cur = nxt;
+        nxt = nn;
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
+            wc[m] = wn[m];
+#pragma unroll
+        for (int i = 0; i < ACH; ++i)
+            aro[i] = aro_n[i];
+        item_rows<ACH, GU>(p, nxt, tid, aro_n);
     }
 }
 
-template <int BM, bool GU>
+template <int BM, bool GU, int SD>
 void run(const ExpertArgs &a, hipStream_t st)
 {
     StreamP p;
@@ -260,6 +343,7 @@ void run(const ExpertArgs &a, hipStream_t st)
     p.tiles = GU ? a.tiles_gu : a.tiles_dc;
     p.ntiles = GU ? a.ntiles_gu : a.ntiles_dc;
     p.items = GU ? a.items_gu : a.items_dc;
+    p.row_tok = a.row_tok;
     p.T = a.T;
     p.H = a.H;
     p.E = a.E;
@@ -268,12 +352,30 @@ void run(const ExpertArgs &a, hipStream_t st)
     p.Is = a.I_shared;
     p.ldh = a.I > a.I_shared ? a.I : a.I_shared;
     const int N = GU ? p.ldh : a.H;
-    p.ntn = (N + WROWS - 1) / WROWS;
+    p.ntn = (N + wrows_of(GU) - 1) / wrows_of(GU);
     const int64_t items = (int64_t)p.ntn * (GU ? a.max_tiles_gu : a.max_tiles_dc);
     if (items == 0)
         return;
-    const unsigned grid = (unsigned)((items + 7) / 8 * 8);
-    expert_stream<BM, GU><<<grid, 256, 0, st>>>(p);
+    // Persistent grid: as many workgroups per XCD as fit at once, never more
+    // than the items an XCD can receive.
+    static int per_cu[2] = {0, 0};
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0, n = 0;
+        (void)hipGetDevice(&dev);
+        (void)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        cus = n > 0 ? n : 256;
+    }
+    int &occ = per_cu[GU ? 1 : 0];
+    if (!occ) {
+        int b = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, expert_stream<BM, GU, SD>, 256, 0) != hipSuccess || b < 1)
+            b = 1;
+        occ = b;
+    }
+    const int64_t per_xcd = (items + 7) / 8;
+    const int64_t slots = std::min<int64_t>(per_xcd, (int64_t)(cus / 8) * occ);
+    expert_stream<BM, GU, SD><<<(unsigned)(slots * 8), 256, 0, st>>>(p, p.items);
 }
 
 }  // namespace
@@ -282,21 +384,36 @@ bool stream_ok(const ExpertArgs &a, bool gu)
 {
     if (a.act != ACT_BF16 || a.wdt != W_BF16)
         return false;
+    // one width for every item of a launch: no shared expert, or one as wide
+    // as the routed experts
+    if (a.I_shared != 0 && a.I_shared != a.I)
+        return false;
     if (gu)
-        return a.H % 256 == 0 && a.I % WROWS == 0 && a.I_shared % WROWS == 0;
-    return a.I % 256 == 0 && a.I_shared % 256 == 0 && a.H % WROWS == 0;
+        return a.H % 256 == 0 && a.I % wrows_of(true) == 0;
+    return a.I % 256 == 0 && a.H % wrows_of(false) == 0;
 }
+
+int stream_wrows(bool gu) { return wrows_of(gu); }
 
 int stream_ntn(const ExpertArgs &a, bool gu)
 {
     if (!stream_ok(a, gu))
         return 0;
     const int N = gu ? (a.I > a.I_shared ? a.I : a.I_shared) : a.H;
-    return (N + WROWS - 1) / WROWS;
+    return (N + wrows_of(gu) - 1) / wrows_of(gu);
 }
 
+// Row-tile size by the mean rows per expert; MOE_STREAM_BM (16, 32, 64 or
+// 128) overrides it for tuning runs (read once per process).
 int stream_bm(const ExpertArgs &a)
 {
+    static const int forced = [] {
+        const char *e = getenv("MOE_STREAM_BM");
+        const int v = e ? atoi(e) : 0;
+        return (v == 16 || v == 32 || v == 64 || v == 128) ? v : 0;
+    }();
+    if (forced)
+        return forced;
     const int64_t avg = (int64_t)a.shape_T * a.k / a.E;
     if (avg <= 16)
         return 16;
@@ -305,28 +422,52 @@ int stream_bm(const ExpertArgs &a)
     return 128;
 }
 
-void launch_stream(const ExpertArgs &a, bool gu, hipStream_t st)
+// Prefetch ring depth in K steps; MOE_STREAM_SD (2, 4 or 8) overrides the
+// default for tuning runs (read once per process).
+static int stream_sd(int bm)
+{
+    static const int forced = [] {
+        const char *e = getenv("MOE_STREAM_SD");
+        const int v = e ? atoi(e) : 0;
+        return (v == 2 || v == 4 || v == 8) ? v : 0;
+    }();
+    if (forced)
+        return forced;
+    return bm >= 128 ? 4 : 8;
+}
+
+template <int BM, bool GU>
+static void run_sd(const ExpertArgs &a, hipStream_t st)
+{
+    const int sd = stream_sd(BM);
+    if (sd == 2)
+        run<BM, GU, 2>(a, st);
+    else if (sd == 4)
+        run<BM, GU, 4>(a, st);
+    else
+        run<BM, GU, 8>(a, st);
+}
+
+template <bool GU>
+static void run_bm(const ExpertArgs &a, hipStream_t st)
 {
     const int bm = stream_bm(a);
-    if (gu) {
-        if (bm == 16)
-            run<16, true>(a, st);
-        else if (bm == 32)
-            run<32, true>(a, st);
-        else if (bm == 64)
-            run<64, true>(a, st);
-        else
-            run<128, true>(a, st);
-    } else {
-        if (bm == 16)
-            run<16, false>(a, st);
-        else if (bm == 32)
-            run<32, false>(a, st);
-        else if (bm == 64)
-            run<64, false>(a, st);
-        else
-            run<128, false>(a, st);
-    }
+    if (bm == 16)
+        run_sd<16, GU>(a, st);
+    else if (bm == 32)
+        run_sd<32, GU>(a, st);
+    else if (bm == 64)
+        run_sd<64, GU>(a, st);
+    else
+        run_sd<128, GU>(a, st);
+}
+
+void launch_stream(const ExpertArgs &a, bool gu, hipStream_t st)
+{
+    if (gu)
+        run_bm<true>(a, st);
+    else
+        run_bm<false>(a, st);
 }
 
 }  // namespace moe

@@ -32,30 +32,33 @@ struct PermuteArgs {
     int32_t *blk;         // [nblk, E] workspace
     int32_t *counts;      // [E + 1]
     int32_t *offsets;     // [E + 2]
-    int32_t *row_src;     // [T*k + T]
+    int32_t *row_src;     // [T*k + T] pair id of each grouped row
+    int32_t *row_tok;     // [T*k + T] token of each grouped row
+    int32_t *row_of;      // [T*k] grouped row of each pair (inverse of row_src)
     Tile *tiles_a;        // tile list for row-block size bm_a
     int32_t *ntiles_a;
     Tile *tiles_b;        // tile list for row-block size bm_b
     int32_t *ntiles_b;
     int bm_a, bm_b;
-    // Optional work-item lists (expert-major, then column tile, then row
-    // tile): item = tile index | column tile << 20, ntn_* column tiles each.
-    uint32_t *items_a, *items_b;
-    int ntn_a, ntn_b;
+    // Optional work-item lists of the streaming GEMMs (expert-major, then
+    // column tile, then row tile): {group, first row, rows, first column}.
+    int4 *items_a, *items_b;
+    int ntn_a, ntn_b, max_tiles_a, max_tiles_b, wrows_a, wrows_b;
     int T, E, k, shared;
 };
 int permute_blocks(int n_pairs);  // number of histogram blocks
 void launch_permute(const PermuteArgs &a, hipStream_t st);
 
 // Grouped gate+up GEMM with the SwiGLU epilogue: h[row] = silu(x_t Wg^T) *
-// (x_t Wu^T) for every grouped row; and the grouped down GEMM with the
-// routing-weight scale writing stage[pair].
+// (x_t Wu^T) for every grouped row; and the grouped down GEMM writing
+// stage[row] = h[row] Wd^T, one staging row per grouped row.
 struct ExpertArgs {
     const void *x;                           // [T, H] act
     const void *w_gate, *w_up, *w_down;      // routed weights (codes for MXFP4)
     const uint8_t *s_gate, *s_up, *s_down;   // MXFP4 scales
     const void *sh_gate, *sh_up, *sh_down;   // shared expert (act dtype)
-    const int32_t *row_src;                  // [rows]
+    const int32_t *row_src;                  // [rows] pair id
+    const int32_t *row_tok;                  // [rows] token
     const int32_t *offsets;                  // [E + 2]
     const float *topk_w;                     // [T*k]
     void *h;                                 // [rows, max(I, I_shared)] act
@@ -64,7 +67,7 @@ struct ExpertArgs {
     const int32_t *ntiles_gu;
     const Tile *tiles_dc;
     const int32_t *ntiles_dc;
-    const uint32_t *items_gu, *items_dc;   // work items of the streaming kernels
+    const int4 *items_gu, *items_dc;       // work items of the streaming kernels
     int max_tiles_gu, max_tiles_dc;
     int T, H, E, k, I, I_shared, act, wdt;
     int shape_T;  // tokens of a full pass: selects the tile shape
@@ -78,6 +81,7 @@ int gemm_bm_dc(const ExpertArgs &a);
 bool stream_ok(const ExpertArgs &a, bool gu);
 int stream_bm(const ExpertArgs &a);
 int stream_ntn(const ExpertArgs &a, bool gu);  // column tiles (0 if not streaming)
+int stream_wrows(bool gu);                     // weight rows per streaming work item
 void launch_stream(const ExpertArgs &a, bool gu, hipStream_t st);
 
 // MXFP4 expert weights (bf16 activations, no shared expert).
@@ -85,9 +89,12 @@ int mxfp4_bm();
 void launch_gate_up_mxfp4(const ExpertArgs &a, hipStream_t st);
 void launch_down_mxfp4(const ExpertArgs &a, hipStream_t st);
 
-// y[t] = sum_j stage[t*k + j] (+ stage[T*k + t]) in j order.
+// y[t] = sum_j w[t*k + j] * stage[row_of[t*k + j]] (+ stage[T*k + t]) in
+// j order: the routing-weight scale and the deterministic combine.
 struct CombineArgs {
     const void *stage;
+    const int32_t *row_of;
+    const float *topk_w;
     void *y;
     int T, H, k, shared, act;
 };

@@ -112,8 +112,8 @@ int check_weights(const moe_shape_t *s, const moe_weights_t *w)
 
 // Workspace layout of one pass of Tc tokens.
 struct Layout {
-    size_t logits, wts, blk, counts, offsets, row_src, tiles_gu, ntiles, tiles_dc, items_gu,
-        items_dc, h, stage, total;
+    size_t logits, wts, blk, counts, offsets, row_src, row_tok, row_of, tiles_gu, ntiles, tiles_dc,
+        items_gu, items_dc, h, stage, total;
     int max_tiles_gu, max_tiles_dc, bm_gu, bm_dc, ntn_gu, ntn_dc;
 };
 
@@ -167,11 +167,13 @@ Layout layout(const moe_shape_t *s, int Tc)
     L.counts = take((size_t)(s->E + 1) * 4);
     L.offsets = take((size_t)(s->E + 2) * 4);
     L.row_src = take((size_t)rows * 4);
+    L.row_tok = take((size_t)rows * 4);
+    L.row_of = take((size_t)pairs * 4);
     L.tiles_gu = take((size_t)L.max_tiles_gu * sizeof(moe::Tile));
     L.ntiles = take(2 * 4);
     L.tiles_dc = take((size_t)L.max_tiles_dc * sizeof(moe::Tile));
-    L.items_gu = take((size_t)L.max_tiles_gu * L.ntn_gu * 4);
-    L.items_dc = take((size_t)L.max_tiles_dc * L.ntn_dc * 4);
+    L.items_gu = take((size_t)L.max_tiles_gu * L.ntn_gu * 16);
+    L.items_dc = take((size_t)L.max_tiles_dc * L.ntn_dc * 16);
     L.h = take((size_t)rows * ldh * esz);
     L.stage = take((size_t)rows * s->H * esz);
     L.total = off;
@@ -271,16 +273,22 @@ int route_pass(const moe_shape_t *s, const moe_weights_t *w, const void *x, int 
     p.counts = (int32_t *)(ws + L.counts);
     p.offsets = (int32_t *)(ws + L.offsets);
     p.row_src = (int32_t *)(ws + L.row_src);
+    p.row_tok = (int32_t *)(ws + L.row_tok);
+    p.row_of = (int32_t *)(ws + L.row_of);
     p.tiles_a = (moe::Tile *)(ws + L.tiles_gu);
     p.ntiles_a = (int32_t *)(ws + L.ntiles);
     p.tiles_b = (moe::Tile *)(ws + L.tiles_dc);
     p.ntiles_b = (int32_t *)(ws + L.ntiles) + 1;
     p.bm_a = L.bm_gu;
     p.bm_b = L.bm_dc;
-    p.items_a = L.ntn_gu ? (uint32_t *)(ws + L.items_gu) : nullptr;
-    p.items_b = L.ntn_dc ? (uint32_t *)(ws + L.items_dc) : nullptr;
+    p.items_a = L.ntn_gu ? (int4 *)(ws + L.items_gu) : nullptr;
+    p.items_b = L.ntn_dc ? (int4 *)(ws + L.items_dc) : nullptr;
     p.ntn_a = L.ntn_gu;
     p.ntn_b = L.ntn_dc;
+    p.max_tiles_a = L.max_tiles_gu;
+    p.max_tiles_b = L.max_tiles_dc;
+    p.wrows_a = moe::stream_wrows(true);
+    p.wrows_b = moe::stream_wrows(false);
     p.T = Tc;
     p.E = s->E;
     p.k = s->top_k;
@@ -363,6 +371,7 @@ int moe_forward(const moe_shape_t *s, const moe_weights_t *w, const void *x, voi
         a.sh_up = w->sh_up;
         a.sh_down = w->sh_down;
         a.row_src = (const int32_t *)(wsb + Lw.row_src);
+        a.row_tok = (const int32_t *)(wsb + Lw.row_tok);
         a.offsets = (const int32_t *)(wsb + Lw.offsets);
         a.topk_w = wts;
         a.h = wsb + Lw.h;
@@ -370,8 +379,8 @@ int moe_forward(const moe_shape_t *s, const moe_weights_t *w, const void *x, voi
         a.tiles_gu = (const moe::Tile *)(wsb + Lw.tiles_gu);
         a.ntiles_gu = (const int32_t *)(wsb + Lw.ntiles);
         a.tiles_dc = (const moe::Tile *)(wsb + Lw.tiles_dc);
-        a.items_gu = (const uint32_t *)(wsb + Lw.items_gu);
-        a.items_dc = (const uint32_t *)(wsb + Lw.items_dc);
+        a.items_gu = (const int4 *)(wsb + Lw.items_gu);
+        a.items_dc = (const int4 *)(wsb + Lw.items_dc);
         a.ntiles_dc = (const int32_t *)(wsb + Lw.ntiles) + 1;
         a.max_tiles_gu = Lw.max_tiles_gu;
         a.max_tiles_dc = Lw.max_tiles_dc;
@@ -389,6 +398,8 @@ int moe_forward(const moe_shape_t *s, const moe_weights_t *w, const void *x, voi
             return rc;
         moe::CombineArgs cb{};
         cb.stage = wsb + Lw.stage;
+        cb.row_of = (const int32_t *)(wsb + Lw.row_of);
+        cb.topk_w = wts;
         cb.y = yc;
         cb.T = n;
         cb.H = s->H;

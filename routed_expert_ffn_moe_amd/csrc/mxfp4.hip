@@ -258,9 +258,7 @@ __global__ __launch_bounds__(64) void expert_mxfp4(MxP p)
             const float hv = silu(acc[0][i]) * acc[NB - 1][i];
             p.out[(int64_t)pos * p.ldh + n] = f2bf(hv);
         } else {
-            const int pr = p.row_src[pos];
-            const float wt = pr < n_pairs ? p.topk_w[pr] : 1.0f;
-            p.out[(int64_t)pr * p.H + n] = f2bf(acc[0][i] * wt);
+            p.out[(int64_t)pos * p.H + n] = f2bf(acc[0][i]);
         }
     }
 }

@@ -52,8 +52,7 @@ __global__ __launch_bounds__(1024) void permute_scan(
     int32_t *__restrict__ blk, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     Tile *__restrict__ tiles_a, int32_t *__restrict__ ntiles_a, Tile *__restrict__ tiles_b,
     int32_t *__restrict__ ntiles_b, int bm_a, int bm_b, int nblk, int E, int n_pairs, int T,
-    int shared, uint32_t *__restrict__ items_a, int ntn_a, uint32_t *__restrict__ items_b,
-    int ntn_b)
+    int shared)
 {
     __shared__ int32_t s_cnt[1025];
     __shared__ int32_t s_ta[1025];
@@ -124,8 +123,7 @@ __global__ __launch_bounds__(1024) void permute_scan(
         for (int b = 0; b < nblk; ++b)
             blk[(int64_t)b * E + e] += o;
     }
-    // Tile lists, and the work items of each list: the tiles of expert g
-    // start at s_g; its items start at ntn * s_g, column tile outer.
+    // Tile lists.
     for (int g = tid; g < G; g += 1024) {
         int cg = g < E ? s_cnt[g] : T;
         int og = s_off[g];
@@ -133,15 +131,6 @@ __global__ __launch_bounds__(1024) void permute_scan(
             tiles_a[t] = Tile{g, og + r};
         for (int r = 0, t = s_tb[g]; r < cg; r += bm_b, ++t)
             tiles_b[t] = Tile{g, og + r};
-        const int na = (cg + bm_a - 1) / bm_a, nb = (cg + bm_b - 1) / bm_b;
-        if (items_a)
-            for (int nt = 0; nt < ntn_a; ++nt)
-                for (int m = 0; m < na; ++m)
-                    items_a[ntn_a * s_ta[g] + nt * na + m] = (uint32_t)(s_ta[g] + m) | ((uint32_t)nt << 20);
-        if (items_b)
-            for (int nt = 0; nt < ntn_b; ++nt)
-                for (int m = 0; m < nb; ++m)
-                    items_b[ntn_b * s_tb[g] + nt * nb + m] = (uint32_t)(s_tb[g] + m) | ((uint32_t)nt << 20);
     }
 }
 
@@ -151,8 +140,10 @@ __global__ __launch_bounds__(1024) void permute_scan(
 // running position in LDS.
 __global__ __launch_bounds__(64) void permute_scatter(const int32_t *__restrict__ idx,
                                                      const int32_t *__restrict__ blk,
-                                                     int32_t *__restrict__ row_src, int n_pairs,
-                                                     int E, int T, int shared)
+                                                     int32_t *__restrict__ row_src,
+                                                     int32_t *__restrict__ row_tok,
+                                                     int32_t *__restrict__ row_of, int n_pairs,
+                                                     int E, int T, int k, int shared)
 {
     extern __shared__ int32_t run[];
     const int lane = threadIdx.x;
@@ -177,6 +168,8 @@ __global__ __launch_bounds__(64) void permute_scatter(const int32_t *__restrict_
         __syncthreads();
         if (valid) {
             row_src[pos] = p;
+            row_tok[pos] = p / k;
+            row_of[p] = pos;
             if (rank == 0)
                 run[e] += __popcll(match);
         }
@@ -184,9 +177,33 @@ __global__ __launch_bounds__(64) void permute_scatter(const int32_t *__restrict_
     }
     // Shared-expert rows follow the routed ones, in token order.
     if (shared && blockIdx.x == 0) {
-        for (int t = lane; t < T; t += 64)
+        for (int t = lane; t < T; t += 64) {
             row_src[n_pairs + t] = n_pairs + t;
+            row_tok[n_pairs + t] = t;
+        }
     }
+}
+
+// Work items of the streaming GEMMs, one thread per (tile, column tile):
+// expert-major, then column tile, then row tile, so that item lists dealt out
+// in contiguous runs keep an expert on one XCD.  The tiles of expert g start
+// at s_g = tile index - its rank inside the expert; its items at ntn * s_g.
+__global__ __launch_bounds__(256) void permute_items(const Tile *__restrict__ tiles,
+                                                     const int32_t *__restrict__ ntiles,
+                                                     const int32_t *__restrict__ offsets, int bm,
+                                                     int ntn, int wrows, int4 *__restrict__ items)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    const int n_t = *ntiles;
+    const int tau = i / ntn, nt = i - tau * ntn;
+    if (tau >= n_t)
+        return;
+    const Tile tl = tiles[tau];
+    const int og = offsets[tl.g], cg = offsets[tl.g + 1] - og;
+    const int rank = (tl.row0 - og) / bm;
+    const int sg = tau - rank;
+    const int na = (cg + bm - 1) / bm;
+    items[ntn * sg + nt * na + rank] = int4{tl.g, tl.row0, min(bm, cg - (tl.row0 - og)), nt * wrows};
 }
 
 void launch_permute(const PermuteArgs &a, hipStream_t st)
@@ -196,11 +213,16 @@ void launch_permute(const PermuteArgs &a, hipStream_t st)
     if (nblk > 0)
         permute_hist<<<nblk, 256, a.E * sizeof(int32_t), st>>>(a.idx, a.blk, n_pairs, a.E);
     permute_scan<<<1, 1024, 0, st>>>(a.blk, a.counts, a.offsets, a.tiles_a, a.ntiles_a, a.tiles_b,
-                                     a.ntiles_b, a.bm_a, a.bm_b, nblk, a.E, n_pairs, a.T, a.shared,
-                                     a.items_a, a.ntn_a, a.items_b, a.ntn_b);
+                                     a.ntiles_b, a.bm_a, a.bm_b, nblk, a.E, n_pairs, a.T, a.shared);
     if (nblk > 0)
-        permute_scatter<<<nblk, 64, a.E * sizeof(int32_t), st>>>(a.idx, a.blk, a.row_src, n_pairs,
-                                                                 a.E, a.T, a.shared);
+        permute_scatter<<<nblk, 64, a.E * sizeof(int32_t), st>>>(
+            a.idx, a.blk, a.row_src, a.row_tok, a.row_of, n_pairs, a.E, a.T, a.k, a.shared);
+    if (a.items_a && a.max_tiles_a > 0)
+        permute_items<<<(a.max_tiles_a * a.ntn_a + 255) / 256, 256, 0, st>>>(
+            a.tiles_a, a.ntiles_a, a.offsets, a.bm_a, a.ntn_a, a.wrows_a, a.items_a);
+    if (a.items_b && a.max_tiles_b > 0)
+        permute_items<<<(a.max_tiles_b * a.ntn_b + 255) / 256, 256, 0, st>>>(
+            a.tiles_b, a.ntiles_b, a.offsets, a.bm_b, a.ntn_b, a.wrows_b, a.items_b);
 }
 
 }  // namespace moe
