@@ -54,6 +54,26 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v)
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// Registers that carry a staged chunk across a loop iteration are held as
+// one vector value: an array there would be placed in scratch memory.
+template <int N>
+using u32v = uint32_t __attribute__((ext_vector_type(4 * N)));
+
+template <int N>
+__device__ __forceinline__ void vset(u32v<N> &r, int i, uint4 t)
+{
+    r[4 * i] = t.x;
+    r[4 * i + 1] = t.y;
+    r[4 * i + 2] = t.z;
+    r[4 * i + 3] = t.w;
+}
+
+template <int N>
+__device__ __forceinline__ uint4 vget(const u32v<N> &r, int i)
+{
+    return uint4{r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]};
+}
+
 // Tile descriptor written by the permutation: group g (expert, or E for the
 // shared expert) and the first grouped row of the tile.
 struct Tile {

@@ -50,11 +50,6 @@ struct StreamP {
     int T, H, E, k, I, Is, ldh, ntn;
 };
 
-// Token chunk registers as one vector value (an array here would be placed
-// in scratch memory by the compiler).
-template <int N>
-using u32v = uint32_t __attribute__((ext_vector_type(4 * N)));
-
 template <int N>
 __device__ __forceinline__ void chunk_store(const u32v<N> &r, uint16_t *dst, const int (&off)[N])
 {
@@ -145,8 +140,13 @@ __device__ __forceinline__ void kstep(const uint16_t *As, int slot, int s4, int 
 // finishes.  Item records are fetched two items ahead and row tokens one item
 // ahead, so no wait on them ever drains the weight stream.  All items of a
 // launch share N and K (the shared expert, if any, has the routed width).
+// Workgroups per CU the register budget is held to: more resident waves hide
+// the LDS and L2 latency that one wave's own schedule cannot.
+constexpr int wg_per_cu(int bm) { return bm <= 16 ? 3 : bm <= 64 ? 2 : 1; }
+
 template <int BM, bool GU, int SD>
-__global__ __launch_bounds__(256) void expert_stream(StreamP p, const int4 *__restrict__ items)
+__global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
+                                                                    const int4 *__restrict__ items)
 {
     constexpr int NB = GU ? 2 : 1;             // weight matrices
     constexpr int CB = GU ? 2 : 4;             // 16-row weight blocks per wave and matrix
@@ -433,7 +433,8 @@ static int stream_sd(int bm)
     }();
     if (forced)
         return forced;
-    return bm >= 128 ? 4 : 8;
+    (void)bm;
+    return 4;  // deeper rings spill under the occupancy bounds (see wg_per_cu)
 }
 
 template <int BM, bool GU>

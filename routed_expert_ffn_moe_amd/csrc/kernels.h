@@ -22,7 +22,8 @@ struct RouterArgs {
     float *w;             // [T, k]
     int T, H, E, k, act;
 };
-void launch_router(const RouterArgs &a, hipStream_t st);
+void launch_router(const RouterArgs &a, hipStream_t st);         // logits + top-k
+void launch_router_logits(const RouterArgs &a, hipStream_t st);  // logits only
 
 // Permutation of one pass: counts, offsets and the grouped order of the
 // (t, j) pairs, plus the GEMM tile lists.  Group E is the shared expert
@@ -48,6 +49,11 @@ struct PermuteArgs {
 };
 int permute_blocks(int n_pairs);  // number of histogram blocks
 void launch_permute(const PermuteArgs &a, hipStream_t st);
+
+// Short passes (route_small.hip): router logits, top-k and the whole
+// permutation in two launches.
+bool route_small_ok(int T, int k, int E);
+void launch_route_small(const RouterArgs &r, const PermuteArgs &a, hipStream_t st);
 
 // Grouped gate+up GEMM with the SwiGLU epilogue: h[row] = silu(x_t Wg^T) *
 // (x_t Wu^T) for every grouped row; and the grouped down GEMM writing

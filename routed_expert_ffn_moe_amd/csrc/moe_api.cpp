@@ -260,7 +260,8 @@ int route_pass(const moe_shape_t *s, const moe_weights_t *w, const void *x, int 
     r.E = s->E;
     r.k = s->top_k;
     r.act = s->act_dtype == MOE_BF16 ? moe::ACT_BF16 : moe::ACT_F32;
-    {
+    const bool small = moe::route_small_ok(Tc, s->top_k, s->E);
+    if (!small) {
         StageScope sc(0, st);
         moe::launch_router(r, st);
     }
@@ -293,7 +294,10 @@ int route_pass(const moe_shape_t *s, const moe_weights_t *w, const void *x, int 
     p.E = s->E;
     p.k = s->top_k;
     p.shared = s->I_shared > 0;
-    {
+    if (small) {
+        StageScope sc(1, st);  // router and permutation in one stage
+        moe::launch_route_small(r, p, st);
+    } else {
         StageScope sc(1, st);
         moe::launch_permute(p, st);
     }

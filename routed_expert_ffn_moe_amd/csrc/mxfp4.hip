@@ -195,6 +195,69 @@ __device__ __forceinline__ void mx_chunk(const uint8_t *const *wrow, const uint8
     }
 }
 
+// Weights of one S=4 chunk (512 K) for the lane: 64 code bytes and 4 scale
+// bytes per matrix.
+template <int NB>
+struct MxChunk {
+    uint4 c[NB][4];
+    uint32_t s[NB];
+};
+
+template <int NB>
+__device__ __forceinline__ void mx_load4(MxChunk<NB> &w, const uint8_t *const *wrow,
+                                         const uint8_t *const *srow, int kc)
+{
+    const int g4 = threadIdx.x >> 4;
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+        const uint8_t *cp = wrow[m] + (kc + 128 * g4) / 2;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            w.c[m][s] = *(const uint4 *)(cp + 16 * s);
+        w.s[m] = *(const uint32_t *)(srow[m] + kc / 32 + 4 * g4);
+    }
+}
+
+template <int NB>
+__device__ __forceinline__ void mx_compute4(const MxChunk<NB> &w, const uint8_t *ahi,
+                                            const uint8_t *alo, const uint8_t *shi,
+                                            const uint8_t *slo, int K, int kc, int ar,
+                                            bool arow_ok, floatx4 *acc)
+{
+    const int g4 = threadIdx.x >> 4;
+    const int nblk = K / 32;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int off = (g4 & 1) * 16;
+        const int k_lo = kc + 32 * (4 * (g4 >> 1) + s) + off;
+        const int k_hi = kc + 32 * (4 * (2 + (g4 >> 1)) + s) + off;
+        intx8 ah = {0, 0, 0, 0, 0, 0, 0, 0}, al = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (arow_ok) {
+            const uint4 h0 = *(const uint4 *)(ahi + ar * K + k_lo);
+            const uint4 h1 = *(const uint4 *)(ahi + ar * K + k_hi);
+            const uint4 l0 = *(const uint4 *)(alo + ar * K + k_lo);
+            const uint4 l1 = *(const uint4 *)(alo + ar * K + k_hi);
+            ah = intx8{(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w,
+                       (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
+            al = intx8{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w,
+                       (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
+        }
+        const int sblk = kc / 32 + 4 * g4 + s;
+        const int sa_h = shi[ar * nblk + sblk];
+        const int sa_l = slo[ar * nblk + sblk];
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+            const uint4 c = w.c[m][s];
+            const intx8 b = {(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+            const int sb = (int)((w.s[m] >> (8 * s)) & 0xFF);
+            acc[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ah, b, acc[m], 0, 4, 0, sa_h,
+                                                                       0, sb);
+            acc[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(al, b, acc[m], 0, 4, 0, sa_l,
+                                                                       0, sb);
+        }
+    }
+}
+
 template <bool GU>
 __global__ __launch_bounds__(64) void expert_mxfp4(MxP p)
 {
@@ -217,8 +280,6 @@ __global__ __launch_bounds__(64) void expert_mxfp4(MxP p)
     uint8_t *alo = ahi + p.cap * K;
     uint8_t *shi = alo + p.cap * K;
     uint8_t *slo = shi + p.cap * (K / 32);
-    stage_activations(p, GU, row0, nrows, K, ahi, alo, shi, slo);
-    __syncthreads();
 
     const int64_t cstride = (int64_t)N * (K / 2), sstride = (int64_t)N * (K / 32);
     const int n = n0 + (lane & 15);
@@ -229,6 +290,17 @@ __global__ __launch_bounds__(64) void expert_mxfp4(MxP p)
         wrow[NB - 1] = p.c1 + g * cstride + (int64_t)n * (K / 2);
         srow[NB - 1] = p.s1 + g * sstride + (int64_t)n * (K / 32);
     }
+    // The first two 512-wide weight chunks go out before the activations are
+    // quantised, so their HBM latency overlaps that work.
+    const int nfull = K / 512;
+    MxChunk<NB> wa, wb;
+    if (nfull > 0) {
+        mx_load4<NB>(wa, wrow, srow, 0);
+        mx_load4<NB>(wb, wrow, srow, min(1, nfull - 1) * 512);
+    }
+    stage_activations(p, GU, row0, nrows, K, ahi, alo, shi, slo);
+    __syncthreads();
+
     const int r = lane & 15;
     const bool rok = r < nrows;
     const int ar = rok ? r : 0;
@@ -237,9 +309,17 @@ __global__ __launch_bounds__(64) void expert_mxfp4(MxP p)
 #pragma unroll
     for (int m = 0; m < NB; ++m)
         acc[m] = floatx4{0, 0, 0, 0};
-    int kc = 0;
-    for (; kc + 512 <= K; kc += 512)
-        mx_chunk<4, NB>(wrow, srow, ahi, alo, shi, slo, K, kc, ar, rok, acc);
+    // Two-chunk register pipeline over the 512-wide chunks (the last reloads
+    // are re-reads of the final chunk, never out of bounds).
+    for (int c = 0; c < nfull; c += 2) {
+        mx_compute4<NB>(wa, ahi, alo, shi, slo, K, c * 512, ar, rok, acc);
+        mx_load4<NB>(wa, wrow, srow, min(c + 2, nfull - 1) * 512);
+        if (c + 1 < nfull) {
+            mx_compute4<NB>(wb, ahi, alo, shi, slo, K, (c + 1) * 512, ar, rok, acc);
+            mx_load4<NB>(wb, wrow, srow, min(c + 3, nfull - 1) * 512);
+        }
+    }
+    int kc = nfull * 512;
     if (kc + 256 <= K) {
         mx_chunk<2, NB>(wrow, srow, ahi, alo, shi, slo, K, kc, ar, rok, acc);
         kc += 256;

@@ -1,0 +1,201 @@
+// Router and permutation for short passes (decode and verify shapes, at most
+// 16 tokens and 256 (token, slot) pairs): two launches instead of seven.
+//
+//  router_small: logits of <= 16 tokens; each workgroup owns 16 experts and
+//                its 4 waves split K in quarters, then add their partial sums
+//                in a fixed order (deterministic).
+//  route_small:  one workgroup: top-k and weights of every token, then the
+//                expert histogram, the prefix sums, the stable grouping of the
+//                pairs, the tile lists and the work items, all in LDS.
+//
+// Pages: "DeepSeek V4.1F Q4 with native DSpark MTP" (decode paragraph: the
+// time went to hundreds of small dispatches per token, and the router was
+// cut from nine dispatches to one; verify rows are 6 at a time).
+#include "common.h"
+#include "kernels.h"
+#include "topk.h"
+
+namespace moe {
+
+constexpr int RS_RING = 8;  // K steps in flight per wave
+
+__global__ __launch_bounds__(256) void router_small(const uint16_t *__restrict__ x,
+                                                    const uint16_t *__restrict__ wr,
+                                                    const float *__restrict__ bias,
+                                                    float *__restrict__ logits, int T, int H, int E)
+{
+    __shared__ float red[4][16][17];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int e0 = blockIdx.x * 16;
+    const int kq = H / 4;  // K quarter of this wave (multiple of 32)
+    const uint16_t *wp = wr + (int64_t)min(e0 + l16, E - 1) * H + wave * kq + lg * 8;
+    const uint16_t *xp = x + (int64_t)min(l16, T - 1) * H + wave * kq + lg * 8;
+    const int nst = kq / 32;
+    uint4 wq[RS_RING], xq[RS_RING];
+#pragma unroll
+    for (int d = 0; d < RS_RING; ++d) {
+        wq[d] = *(const uint4 *)(wp + min(d, nst - 1) * 32);
+        xq[d] = *(const uint4 *)(xp + min(d, nst - 1) * 32);
+    }
+    floatx4 acc = {0, 0, 0, 0};
+    for (int s0 = 0; s0 < nst; s0 += RS_RING) {
+#pragma unroll
+        for (int d = 0; d < RS_RING; ++d) {
+            const int s = s0 + d;
+            const bf16x8 wf = as_bf16x8(wq[d]), xf = as_bf16x8(xq[d]);
+            const int nx = min(s + RS_RING, nst - 1) * 32;
+            wq[d] = *(const uint4 *)(wp + nx);
+            xq[d] = *(const uint4 *)(xp + nx);
+            if (s < nst)
+                acc = mfma16(wf, xf, acc);
+        }
+    }
+    // C[expert 4*lg + i][token l16]
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        red[wave][4 * lg + i][l16] = acc[i];
+    __syncthreads();
+    if (tid < 256) {
+        const int er = tid >> 4, t = tid & 15;  // 16 experts x 16 tokens
+        const int e = e0 + er;
+        if (t < T && e < E) {
+            float v = ((red[0][er][t] + red[1][er][t]) + red[2][er][t]) + red[3][er][t];
+            logits[(int64_t)t * E + e] = v + (bias ? bias[e] : 0.0f);
+        }
+    }
+}
+
+__global__ __launch_bounds__(1024) void route_small(
+    const float *__restrict__ logits, int32_t *__restrict__ idx, float *__restrict__ w, int T,
+    int E, int k, int shared, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ row_src, int32_t *__restrict__ row_tok, int32_t *__restrict__ row_of,
+    Tile *__restrict__ tiles_a, int32_t *__restrict__ ntiles_a, Tile *__restrict__ tiles_b,
+    int32_t *__restrict__ ntiles_b, int bm_a, int bm_b, int4 *__restrict__ items_a, int ntn_a,
+    int wrows_a, int4 *__restrict__ items_b, int ntn_b, int wrows_b)
+{
+    __shared__ int s_idx[256];
+    __shared__ int s_cnt[1025], s_off[1025], s_ta[1025], s_tb[1025];
+    __shared__ int s_warp[3][16];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int P = T * k;
+    const int G = E + (shared ? 1 : 0);
+
+    // 1. top-k and weights, one wave per token
+    for (int t = wv; t < T; t += 16)
+        wave_topk(logits + (int64_t)t * E, E, k, idx + (int64_t)t * k, w + (int64_t)t * k,
+                  s_idx + t * k);
+    __syncthreads();
+
+    // 2. pairs per group
+    for (int g = tid; g < G; g += 1024) {
+        int c = 0;
+        if (g < E) {
+            for (int q = 0; q < P; ++q)
+                c += s_idx[q] == g;
+        } else {
+            c = T;
+        }
+        s_cnt[g] = c;
+    }
+    __syncthreads();
+
+    // 3. exclusive prefix sums of rows and of the tiles of each list
+    const int c = tid < G ? s_cnt[tid] : 0;
+    const int va = tid < G ? (c + bm_a - 1) / bm_a : 0;
+    const int vb = tid < G ? (c + bm_b - 1) / bm_b : 0;
+    int ic = c, ia = va, ib = vb;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int tc = __shfl_up(ic, off), ta = __shfl_up(ia, off), tb = __shfl_up(ib, off);
+        if (lane >= off) {
+            ic += tc;
+            ia += ta;
+            ib += tb;
+        }
+    }
+    if (lane == 63) {
+        s_warp[0][wv] = ic;
+        s_warp[1][wv] = ia;
+        s_warp[2][wv] = ib;
+    }
+    __syncthreads();
+    int pc = 0, pa = 0, pb = 0;
+    for (int q = 0; q < wv; ++q) {
+        pc += s_warp[0][q];
+        pa += s_warp[1][q];
+        pb += s_warp[2][q];
+    }
+    const int exc = pc + ic - c, exa = pa + ia - va, exb = pb + ib - vb;
+    if (tid < G) {
+        counts[tid] = c;
+        offsets[tid] = exc;
+        s_off[tid] = exc;
+        s_ta[tid] = exa;
+        s_tb[tid] = exb;
+    }
+    if (tid == G - 1) {
+        offsets[G] = exc + c;
+        *ntiles_a = exa + va;
+        *ntiles_b = exb + vb;
+    }
+    if (!shared && tid == 0)
+        offsets[E + 1] = P;
+    __syncthreads();
+
+    // 4. stable grouping: rank of pair p among earlier pairs of its expert
+    if (tid < P) {
+        const int e = s_idx[tid];
+        int rank = 0;
+        for (int q = 0; q < tid; ++q)
+            rank += s_idx[q] == e;
+        const int pos = s_off[e] + rank;
+        row_src[pos] = tid;
+        row_tok[pos] = tid / k;
+        row_of[tid] = pos;
+    }
+    if (shared && tid < T) {
+        row_src[P + tid] = P + tid;
+        row_tok[P + tid] = tid;
+    }
+
+    // 5. tile lists and work items, one thread per group
+    for (int g = tid; g < G; g += 1024) {
+        const int cg = s_cnt[g], og = s_off[g];
+        if (cg == 0)
+            continue;
+        const int na = (cg + bm_a - 1) / bm_a, nb = (cg + bm_b - 1) / bm_b;
+        for (int m = 0; m < na; ++m) {
+            tiles_a[s_ta[g] + m] = Tile{g, og + m * bm_a};
+            if (items_a)
+                for (int nt = 0; nt < ntn_a; ++nt)
+                    items_a[ntn_a * s_ta[g] + nt * na + m] =
+                        int4{g, og + m * bm_a, min(bm_a, cg - m * bm_a), nt * wrows_a};
+        }
+        for (int m = 0; m < nb; ++m) {
+            tiles_b[s_tb[g] + m] = Tile{g, og + m * bm_b};
+            if (items_b)
+                for (int nt = 0; nt < ntn_b; ++nt)
+                    items_b[ntn_b * s_tb[g] + nt * nb + m] =
+                        int4{g, og + m * bm_b, min(bm_b, cg - m * bm_b), nt * wrows_b};
+        }
+    }
+}
+
+bool route_small_ok(int T, int k, int E) { return T <= 16 && T * k <= 256 && E <= 1023; }
+
+void launch_route_small(const RouterArgs &r, const PermuteArgs &a, hipStream_t st)
+{
+    if (r.act == ACT_BF16 && r.E % 16 == 0 && r.H % 128 == 0) {
+        router_small<<<r.E / 16, 256, 0, st>>>((const uint16_t *)r.x, (const uint16_t *)r.wr,
+                                               r.bias, r.logits, r.T, r.H, r.E);
+    } else {
+        launch_router_logits(r, st);
+    }
+    route_small<<<1, 1024, 0, st>>>(r.logits, r.idx, r.w, r.T, r.E, r.k, a.shared, a.counts,
+                                    a.offsets, a.row_src, a.row_tok, a.row_of, a.tiles_a,
+                                    a.ntiles_a, a.tiles_b, a.ntiles_b, a.bm_a, a.bm_b, a.items_a,
+                                    a.ntn_a, a.wrows_a, a.items_b, a.ntn_b, a.wrows_b);
+}
+
+}  // namespace moe

@@ -7,6 +7,7 @@
 // never rounded to bf16; selection is on the logits, ties to the lower index.
 #include "common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -58,6 +59,105 @@ __global__ __launch_bounds__(64 * WN) void router_logits_bf16(
     }
 }
 
+// bf16 logits for T > 16: a workgroup owns RT tokens x 64 experts.  The
+// token rows are staged in LDS in double-buffered 128-wide K chunks; each wave
+// streams its 16 expert rows from global memory through an 8-step register
+// ring (no barrier on that path).  The MFMA takes the expert rows as its A
+// operand, so a lane ends up with 4 consecutive experts of one token and
+// stores them as one 16-byte word.  Every logit is the sequential sum over K
+// in 32-wide MFMA steps, whatever RT and the grid are.
+constexpr int RKC = 128;        // K chunk staged in LDS
+constexpr int RLD = RKC + 8;    // padded LDS row (bf16)
+constexpr int RSD = 8;          // weight prefetch ring (K steps)
+
+template <int RT>
+__global__ __launch_bounds__(256) void router_gemm(const uint16_t *__restrict__ x,
+                                                   const uint16_t *__restrict__ wr,
+                                                   const float *__restrict__ bias,
+                                                   float *__restrict__ logits, int T, int H, int E)
+{
+    constexpr int MB = RT / 16;              // token blocks
+    constexpr int XCH = RT * (RKC / 8) / 256; // 16-byte token chunks per thread
+    static_assert(XCH >= 1, "token staging");
+    __shared__ __attribute__((aligned(16))) uint16_t sX[2][RT * RLD];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int t0 = blockIdx.y * RT, e0 = blockIdx.x * 64 + wave * 16;
+    // expert row of this lane: MFMA row l16 -> expert e0 + l16
+    const uint16_t *wp = wr + (int64_t)min(e0 + l16, E - 1) * H + lg * 8;
+    int xo[XCH], so[XCH];
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+        const int q = tid + 256 * i, r = q >> 4, c8 = q & 15;
+        xo[i] = min(t0 + r, T - 1) * H + c8 * 8;
+        so[i] = r * RLD + c8 * 8;
+    }
+    const int nsteps = H / 32, nchunks = H / RKC;  // nchunks even
+    uint4 bq[RSD];
+#pragma unroll
+    for (int d = 0; d < RSD; ++d)
+        bq[d] = *(const uint4 *)(wp + min(d, nsteps - 1) * 32);
+    u32v<XCH> ra;
+#pragma unroll
+    for (int i = 0; i < XCH; ++i)
+        vset<XCH>(ra, i, *(const uint4 *)(x + xo[i]));
+#pragma unroll
+    for (int i = 0; i < XCH; ++i)
+        *(uint4 *)(&sX[0][so[i]]) = vget<XCH>(ra, i);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < XCH; ++i)
+        vset<XCH>(ra, i, *(const uint4 *)(x + xo[i] + min(1, nchunks - 1) * RKC));
+    __builtin_amdgcn_sched_barrier(0);
+    floatx4 acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        acc[mb] = floatx4{0, 0, 0, 0};
+    int buf = 0;
+    for (int c = 0; c < nchunks; c += 2) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int cc = c + h;
+            const uint16_t *Xs = sX[buf];
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const int step = cc * 4 + s4;
+                const bf16x8 wf = as_bf16x8(bq[h * 4 + s4]);
+                bq[h * 4 + s4] = *(const uint4 *)(wp + min(step + RSD, nsteps - 1) * 32);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const bf16x8 tf =
+                        as_bf16x8(*(const uint4 *)(Xs + (mb * 16 + l16) * RLD + s4 * 32 + lg * 8));
+                    acc[mb] = mfma16(wf, tf, acc[mb]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < XCH; ++i)
+                *(uint4 *)(&sX[buf ^ 1][so[i]]) = vget<XCH>(ra, i);
+            __syncthreads();
+            buf ^= 1;
+#pragma unroll
+            for (int i = 0; i < XCH; ++i)
+                vset<XCH>(ra, i, *(const uint4 *)(x + xo[i] + min(cc + 2, nchunks - 1) * RKC));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // lane: experts e0 + 4*lg .. +3 of token mb*16 + l16
+    const int e = e0 + 4 * lg;
+    if (e >= E)
+        return;
+    const float4 bv = bias ? float4{bias[e], bias[e + 1], bias[e + 2], bias[e + 3]}
+                           : float4{0, 0, 0, 0};
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int t = t0 + mb * 16 + l16;
+        if (t < T)
+            *(float4 *)(logits + (int64_t)t * E + e) =
+                float4{acc[mb][0] + bv.x, acc[mb][1] + bv.y, acc[mb][2] + bv.z, acc[mb][3] + bv.w};
+    }
+}
+
 // fp32 logits: one thread per (token, expert), plain dot product.
 __global__ __launch_bounds__(256) void router_logits_f32(
     const float *__restrict__ x, const float *__restrict__ wr,
@@ -75,84 +175,33 @@ __global__ __launch_bounds__(256) void router_logits_f32(
     logits[i] = acc + (bias ? bias[e] : 0.0f);
 }
 
-// (value, index) order of the selection: larger logit first, equal logits by
-// lower expert index.
-__device__ __forceinline__ bool better(float va, int ia, float vb, int ib)
-{
-    return va > vb || (va == vb && ia < ib);
-}
-
-// Top-k and weights: one wave per token.  Lane l holds logits l, l+64, ...;
-// k rounds of a wave-wide arg-max remove one expert each.
+// Top-k and weights: one wave per token (see wave_topk).
 __global__ __launch_bounds__(256) void router_topk(
     const float *__restrict__ logits, int32_t *__restrict__ idx, float *__restrict__ w,
     int T, int E, int k)
 {
-    const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T)
         return;
-    const int per = (E + 63) / 64;  // <= 16
-    float v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        int e = lane + 64 * i;
-        v[i] = (i < per && e < E) ? logits[(int64_t)t * E + e] : -INFINITY;
-        if (v[i] != v[i])  // NaN logits rank last; indices stay valid
-            v[i] = -INFINITY;
-    }
-    float sel_v[16];
-    int sel_i[16];
-    for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            int e = lane + 64 * i;
-            if (i < per && e < E && better(v[i], e, bv, bi)) {
-                bv = v[i];
-                bi = e;
-            }
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            float ov = __shfl_xor(bv, off);
-            int oi = __shfl_xor(bi, off);
-            if (better(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        sel_v[j] = bv;
-        sel_i[j] = bi;
-        if ((bi & 63) == lane) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (i == (bi >> 6))
-                    v[i] = -INFINITY;
-        }
-    }
-    // Softmax over the selected logits (the full softmax renormalised).
-    const float m = sel_v[0];
-    float z = 0.0f;
-    float q[16];
-    for (int j = 0; j < k; ++j) {
-        q[j] = expf(sel_v[j] - m);
-        z += q[j];
-    }
-    for (int j = 0; j < k; ++j) {
-        if (lane == j) {
-            idx[(int64_t)t * k + j] = sel_i[j];
-            w[(int64_t)t * k + j] = q[j] / z;
-        }
-    }
+    wave_topk(logits + (int64_t)t * E, E, k, idx + (int64_t)t * k, w + (int64_t)t * k, nullptr);
 }
 
-void launch_router(const RouterArgs &a, hipStream_t st)
+void launch_router_logits(const RouterArgs &a, hipStream_t st)
 {
     if (a.T == 0)
         return;
-    if (a.act == ACT_BF16) {
+    if (a.act == ACT_BF16 && a.T > 16 && a.E % 64 == 0 && a.H % 256 == 0) {
+        // 64 tokens per workgroup for long chunks, 32 otherwise (more workgroups)
+        if (a.T >= 4096) {
+            dim3 grid(a.E / 64, (a.T + 63) / 64);
+            router_gemm<64><<<grid, 256, 0, st>>>((const uint16_t *)a.x, (const uint16_t *)a.wr,
+                                                 a.bias, a.logits, a.T, a.H, a.E);
+        } else {
+            dim3 grid(a.E / 64, (a.T + 31) / 32);
+            router_gemm<32><<<grid, 256, 0, st>>>((const uint16_t *)a.x, (const uint16_t *)a.wr,
+                                                 a.bias, a.logits, a.T, a.H, a.E);
+        }
+    } else if (a.act == ACT_BF16) {
         if (a.T <= 64) {
             dim3 grid((a.E + 15) / 16, (a.T + 31) / 32);
             router_logits_bf16<1><<<grid, 64, 0, st>>>((const uint16_t *)a.x, (const uint16_t *)a.wr,
@@ -167,6 +216,13 @@ void launch_router(const RouterArgs &a, hipStream_t st)
         router_logits_f32<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
             (const float *)a.x, (const float *)a.wr, a.bias, a.logits, a.T, a.H, a.E);
     }
+}
+
+void launch_router(const RouterArgs &a, hipStream_t st)
+{
+    if (a.T == 0)
+        return;
+    launch_router_logits(a, st);
     router_topk<<<(a.T + 3) / 4, 256, 0, st>>>(a.logits, a.idx, a.w, a.T, a.E, a.k);
 }
 
