@@ -53,7 +53,8 @@ void launch_permute(const PermuteArgs &a, hipStream_t st);
 // Short passes (route_small.hip): router logits, top-k and the whole
 // permutation in two launches.
 bool route_small_ok(int T, int k, int E);
-void launch_route_small(const RouterArgs &r, const PermuteArgs &a, hipStream_t st);
+void launch_router_small(const RouterArgs &r, hipStream_t st);  // logits only
+void launch_route_small(const RouterArgs &r, const PermuteArgs &a, hipStream_t st);  // top-k + permutation
 
 // Grouped gate+up GEMM with the SwiGLU epilogue: h[row] = silu(x_t Wg^T) *
 // (x_t Wu^T) for every grouped row; and the grouped down GEMM writing

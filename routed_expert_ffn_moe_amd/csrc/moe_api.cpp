@@ -261,9 +261,12 @@ int route_pass(const moe_shape_t *s, const moe_weights_t *w, const void *x, int 
     r.k = s->top_k;
     r.act = s->act_dtype == MOE_BF16 ? moe::ACT_BF16 : moe::ACT_F32;
     const bool small = moe::route_small_ok(Tc, s->top_k, s->E);
-    if (!small) {
+    {
         StageScope sc(0, st);
-        moe::launch_router(r, st);
+        if (small)
+            moe::launch_router_small(r, st);  // top-k moves into the permutation pass
+        else
+            moe::launch_router(r, st);
     }
     int rc = launched("router");
     if (rc)
@@ -295,7 +298,7 @@ int route_pass(const moe_shape_t *s, const moe_weights_t *w, const void *x, int 
     p.k = s->top_k;
     p.shared = s->I_shared > 0;
     if (small) {
-        StageScope sc(1, st);  // router and permutation in one stage
+        StageScope sc(1, st);  // top-k and the permutation
         moe::launch_route_small(r, p, st);
     } else {
         StageScope sc(1, st);

@@ -184,14 +184,17 @@ __global__ __launch_bounds__(1024) void route_small(
 
 bool route_small_ok(int T, int k, int E) { return T <= 16 && T * k <= 256 && E <= 1023; }
 
-void launch_route_small(const RouterArgs &r, const PermuteArgs &a, hipStream_t st)
+void launch_router_small(const RouterArgs &r, hipStream_t st)
 {
-    if (r.act == ACT_BF16 && r.E % 16 == 0 && r.H % 128 == 0) {
+    if (r.act == ACT_BF16 && r.E % 16 == 0 && r.H % 128 == 0)
         router_small<<<r.E / 16, 256, 0, st>>>((const uint16_t *)r.x, (const uint16_t *)r.wr,
                                                r.bias, r.logits, r.T, r.H, r.E);
-    } else {
+    else
         launch_router_logits(r, st);
-    }
+}
+
+void launch_route_small(const RouterArgs &r, const PermuteArgs &a, hipStream_t st)
+{
     route_small<<<1, 1024, 0, st>>>(r.logits, r.idx, r.w, r.T, r.E, r.k, a.shared, a.counts,
                                     a.offsets, a.row_src, a.row_tok, a.row_of, a.tiles_a,
                                     a.ntiles_a, a.tiles_b, a.ntiles_b, a.bm_a, a.bm_b, a.items_a,

@@ -25,6 +25,7 @@ if not _gpu_ready():
     pytest.skip("no GPU visible", allow_module_level=True)
 
 import harness as hx  # noqa: E402
+import routed_expert_ffn_moe_amd as moe  # noqa: E402
 
 _LAYERS = {}
 
@@ -157,3 +158,40 @@ def test_zero_tokens_is_a_no_op():
     xd = torch.empty((0, c["H"]), dtype=torch.bfloat16, device="cuda")
     y, idx, w = g.forward(xd)
     assert y.shape == (0, c["H"])
+
+
+@pytest.mark.parametrize("name", ["c4_t6", "c1"])
+def test_graph_replay_matches_eager(name):
+    """The layer captured once into a HIP graph and replayed on new inputs
+    (eager work and synchronisation between replays) equals the eager call."""
+    say("[graph] config", name)
+    c, g = layer(name)
+    T = c["T"]
+    shape = g.shape(T)
+    ws = torch.empty(max(moe.moe_workspace_bytes(shape), 256), dtype=torch.uint8, device="cuda")
+    xs = []
+    for r in range(3):
+        cr = dict(c, seed=c["seed"] + 500 + r)
+        xs.append(hx.act_torch(hx.margin_x(cr, g.lay), c["act"], "cuda"))
+    x_in = torch.empty_like(xs[0])
+    y = torch.empty_like(x_in)
+    idx = torch.empty((T, c["top_k"]), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, c["top_k"]), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    x_in.copy_(xs[0])
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        moe.moe_forward(shape, g.weights, x_in, y, idx, w, ws)  # warm-up outside capture
+        s.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            moe.moe_forward(shape, g.weights, x_in, y, idx, w, ws)
+    torch.cuda.synchronize()
+    for r in (1, 2, 0, 1):
+        x_in.copy_(xs[r])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        y_e, i_e, w_e = g.forward(xs[r])
+        assert torch.equal(idx, i_e) and torch.equal(w, w_e)
+        assert torch.equal(y, y_e)
