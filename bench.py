@@ -91,11 +91,15 @@ class Workload:
             rw = (rw.view(torch.int16).view(torch.bfloat16) if c["act"] == "bf16" else rw).to(dev)
             rb = None if lay.router_bias is None else torch.from_numpy(lay.router_bias).to(dev)
             self._keep += [rw, rb]
-            self.weights.append(moe.make_weights(rw, lay.w_gate, lay.w_up, lay.w_down,
-                                                 router_bias=rb, s_gate=lay.s_gate,
-                                                 s_up=lay.s_up, s_down=lay.s_down,
-                                                 sh_gate=lay.sh_gate, sh_up=lay.sh_up,
-                                                 sh_down=lay.sh_down))
+            wg, wu, wd = lay.w_gate, lay.w_up, lay.w_down
+            sg, su, sd = lay.s_gate, lay.s_up, lay.s_down
+            if c["w"] == "mxfp4":  # one-time repack into the layout the kernels read
+                (wg, sg), (wu, su), (wd, sd) = (moe.pack_mxfp4(wg, sg), moe.pack_mxfp4(wu, su),
+                                                moe.pack_mxfp4(wd, sd))
+                self._keep += [wg, wu, wd, sg, su, sd]
+            self.weights.append(moe.make_weights(rw, wg, wu, wd, router_bias=rb, s_gate=sg,
+                                                 s_up=su, s_down=sd, sh_gate=lay.sh_gate,
+                                                 sh_up=lay.sh_up, sh_down=lay.sh_down))
         self.shape = moe.make_shape(c["T"], c["H"], c["E"], c["top_k"], c["I"], c["I_shared"],
                                     0, c["act"], c["w"])
         nb = moe.moe_workspace_bytes(self.shape)

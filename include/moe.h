@@ -27,13 +27,26 @@
  *   router_bias [E]                 float, or NULL
  *   w_gate, w_up [E, I, H]          w_dtype
  *   w_down [E, H, I]                w_dtype
- *     MXFP4 (OCP MX v1.0): codes [E, I, H/2] / [E, H, I/2], two E2M1 codes
- *     per byte, even element in the low nibble; s_* E8M0 scales
- *     [E, I, H/32] / [E, H, I/32], one per 32 consecutive K elements.
+ *     MXFP4 (OCP MX v1.0): the matrices as moe_pack_mxfp4 lays them out
+ *     (below), from the OCP row-major form: codes [E, N, K/2], two E2M1
+ *     codes per byte, even element in the low nibble, and E8M0 scales
+ *     [E, N, K/32], one per 32 consecutive K elements ([N, K] = [I, H] for
+ *     gate and up, [H, I] for down).
  *   sh_gate, sh_up [I_shared, H], sh_down [H, I_shared]   act_dtype
  *   topk_idx [T, top_k] int32, topk_w [T, top_k] float
  *
+ * Packed MXFP4 (what the kernels read: each wave's weights are whole
+ * contiguous kilobytes).  Rows go in blocks of 16 (n = 16*nb + r) and K in
+ * steps of 128 (q = K/128 steps); the lane index l = r + 16*b, b = 0..3:
+ *   codes  [E][N/16][q][64 lanes][16 B]: lane l of step s holds the 32 codes
+ *          of row n at K = 128*s + 32*b .. +31 (OCP byte order);
+ *   scales [E][N/16][64 lanes][q]: byte s of lane l is the scale of row n
+ *          at K = 128*s + 32*b .. +31.
+ * The packed matrices have the same sizes as the OCP ones.
+ *
  * Supported combinations: act F32 with w F32; act BF16 with w BF16 or MXFP4.
+ * MXFP4 needs H and I multiples of 128, at most 4096, and no shared expert
+ * (MOE_EINVAL / MOE_EUNSUPPORTED otherwise).
  * Every pointer except router_bias, topk_w and the unused ones is a device
  * pointer, 16-byte aligned.  The caller owns all memory; the library
  * allocates nothing per call and keeps no state between calls other than
@@ -109,6 +122,15 @@ int moe_route(const moe_shape_t *shape, const moe_weights_t *w,
               const void *x, int32_t *topk_idx, float *topk_w,
               int32_t *counts, int32_t *offsets, int32_t *row_src,
               void *ws, size_t ws_bytes, void *stream);
+
+/* Repack E MXFP4 matrices of N rows and K columns (N a multiple of 16, K of
+ * 128) from the OCP row-major form (codes [E, N, K/2], scales [E, N, K/32])
+ * into the layout moe_forward reads (above); E * N * K / 2 code bytes and
+ * E * N * K / 32 scale bytes out.  Device pointers, 16-byte aligned, the
+ * outputs not overlapping the inputs; asynchronous on `stream`.  A one-time
+ * step when weights are loaded.  MOE_EINVAL on bad sizes or pointers. */
+int moe_pack_mxfp4(int E, int N, int K, const void *codes, const uint8_t *scales,
+                   void *codes_out, uint8_t *scales_out, void *stream);
 
 /* Stage timing for measurement (not needed for computing).  While enabled,
  * moe_forward records a pair of HIP events on its stream around each of its

@@ -18,7 +18,8 @@ __all__ = [
     "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_OK", "MOE_EINVAL", "MOE_EWORKSPACE",
     "MOE_EUNSUPPORTED", "MOE_EHIP", "MoeError", "moe_shape_t", "moe_weights_t", "make_shape",
     "make_weights", "moe_workspace_bytes", "moe_forward", "moe_route", "moe_strerror",
-    "moe_last_error", "moe_stage_timing_enable", "moe_stage_timing_read", "STAGES",
+    "moe_last_error", "moe_stage_timing_enable", "moe_stage_timing_read", "moe_pack_mxfp4",
+    "pack_mxfp4", "STAGES",
     "lib_path", "load",
 ]
 
@@ -75,6 +76,8 @@ def load() -> ctypes.CDLL:
         lib.moe_stage_timing_enable.argtypes = [ctypes.c_int]
         lib.moe_stage_timing_read.restype = ctypes.c_int
         lib.moe_stage_timing_read.argtypes = [P, ctypes.c_int, P]
+        lib.moe_pack_mxfp4.restype = ctypes.c_int
+        lib.moe_pack_mxfp4.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
         _lib = lib
     return _lib
 
@@ -144,6 +147,22 @@ def moe_route(shape, weights, x, topk_idx, topk_w, counts, offsets, row_src, ws,
     _check(load().moe_route(ctypes.byref(shape), ctypes.byref(weights.c), _ptr(x),
                             _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets),
                             _ptr(row_src), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_pack_mxfp4(E, N, K, codes, scales, codes_out, scales_out, stream=None) -> None:
+    """Repack OCP row-major MXFP4 matrices into the layout moe_forward reads."""
+    _check(load().moe_pack_mxfp4(E, N, K, _ptr(codes), _ptr(scales), _ptr(codes_out),
+                                 _ptr(scales_out), _stream(stream)))
+
+
+def pack_mxfp4(codes, scales, stream=None):
+    """Packed copies of codes [E, N, K/2] and scales [E, N, K/32] (uint8 device tensors)."""
+    import torch
+    E, N, K2 = codes.shape
+    out_c = torch.empty_like(codes)
+    out_s = torch.empty_like(scales)
+    moe_pack_mxfp4(E, N, 2 * K2, codes, scales, out_c, out_s, stream)
+    return out_c, out_s
 
 
 STAGES = ("router", "permute", "gate_up", "down", "combine")

@@ -95,6 +95,10 @@ void launch_stream(const ExpertArgs &a, bool gu, hipStream_t st);
 int mxfp4_bm();
 void launch_gate_up_mxfp4(const ExpertArgs &a, hipStream_t st);
 void launch_down_mxfp4(const ExpertArgs &a, hipStream_t st);
+// OCP row-major MXFP4 (codes [E, N, K/2], scales [E, N, K/32]) into the
+// packed layout the MXFP4 kernels read.
+void launch_pack_mxfp4(int E, int N, int K, const uint8_t *codes, const uint8_t *scales,
+                       uint8_t *codes_out, uint8_t *scales_out, hipStream_t st);
 
 // y[t] = sum_j w[t*k + j] * stage[row_of[t*k + j]] (+ stage[T*k + t]) in
 // j order: the routing-weight scale and the deterministic combine.

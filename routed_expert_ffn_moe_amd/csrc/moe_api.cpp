@@ -79,6 +79,8 @@ int check_shape(const moe_shape_t *s)
     }
     if (mx && (s->H % 128 || s->I % 128))
         return fail(MOE_EINVAL, "MXFP4 needs H and I multiples of 128");
+    if (mx && (s->H > 4096 || s->I > 4096))  // activation tile staged in LDS
+        return fail(MOE_EUNSUPPORTED, "MXFP4 supports H and I up to 4096");
     if (mx && s->I_shared)
         return fail(MOE_EUNSUPPORTED, "MXFP4 with a shared expert is not supported");
     return MOE_OK;
@@ -466,6 +468,29 @@ int moe_route(const moe_shape_t *s, const moe_weights_t *w, const void *x, int32
                                   hipMemcpyDeviceToDevice, st) != hipSuccess)
         return launched("copy row_src");
     return MOE_OK;
+}
+
+int moe_pack_mxfp4(int E, int N, int K, const void *codes, const uint8_t *scales, void *codes_out,
+                   uint8_t *scales_out, void *stream)
+{
+    if (E < 1 || N < 16 || N % 16 || K < 128 || K % 128)
+        return fail(MOE_EINVAL, "moe_pack_mxfp4: E >= 1, N a multiple of 16, K of 128");
+    if (!codes || !scales || !codes_out || !scales_out)
+        return fail(MOE_EINVAL, "moe_pack_mxfp4: NULL pointer");
+    if (!aligned16(codes) || !aligned16(scales) || !aligned16(codes_out) || !aligned16(scales_out))
+        return fail(MOE_EINVAL, "moe_pack_mxfp4: pointer not 16-byte aligned");
+    const size_t cb = (size_t)E * N * (K / 2), sb = (size_t)E * N * (K / 32);
+    auto overlap = [](const void *a, size_t na, const void *b, size_t nb) {
+        const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+        return x < y + nb && y < x + na;
+    };
+    if (overlap(codes_out, cb, codes, cb) || overlap(codes_out, cb, scales, sb) ||
+        overlap(scales_out, sb, codes, cb) || overlap(scales_out, sb, scales, sb) ||
+        overlap(codes_out, cb, scales_out, sb))
+        return fail(MOE_EINVAL, "moe_pack_mxfp4: outputs overlap the inputs or each other");
+    moe::launch_pack_mxfp4(E, N, K, (const uint8_t *)codes, scales, (uint8_t *)codes_out,
+                           scales_out, (hipStream_t)stream);
+    return launched("moe_pack_mxfp4");
 }
 
 const char *moe_strerror(int code)

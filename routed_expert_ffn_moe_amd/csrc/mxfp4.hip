@@ -10,12 +10,20 @@
 // codes, two per byte with the even element in the low nibble, one E8M0
 // scale per 32 elements along K.
 //
-// Weight-stationary design: one wave owns one tile of the permutation (one
-// expert's rows, at most 16 and at most T) and 16 output columns per weight
-// matrix; every weight byte is read from HBM exactly once per tile.  The fp4
-// weights are the MFMA's B operand with their own E8M0 scales.  The bf16
-// activations are split into two MXFP8 (E4M3) operands, hi = fp8(x / 2^e)
-// and lo = fp8((x / 2^e - hi) * 16) with scales 2^e and 2^(e-4) per 32-block,
+// Weight-stationary design: a workgroup owns one tile of the permutation
+// (one expert's rows, at most 16 and at most T) and NW*CPW*16 output columns
+// per weight matrix; each of its waves owns CPW blocks of 16 columns.  A wave
+// issues the loads of its whole weight slice (K in slabs of up to 2048) before
+// anything else, so a launch has nearly all of its weight bytes in flight at
+// once; meanwhile the workgroup quantises the tile's activation rows into
+// LDS once for all its waves.  Every weight byte is read from HBM exactly once.
+// The weights are read in the packed layout (moe_pack_mxfp4): one MFMA step
+// of a 16-row block is a contiguous kilobyte, 16 bytes per lane, so every
+// load instruction of a wave fetches whole cache lines.
+//
+// The fp4 weights are the MFMA's B operand with their own E8M0 scales.  The
+// bf16 activations are split into two MXFP8 (E4M3) operands, hi = fp8(x/2^e)
+// and lo = fp8((x/2^e - hi) * 16) with scales 2^e and 2^(e-4) per 32-block,
 // e = floor(log2 amax) - 7; two MFMAs (hi, lo) share the weight operand and
 // reproduce x to about 2^-8 relative, the precision of bf16 itself.
 //
@@ -23,12 +31,11 @@
 // lane l holds column l%16 and K elements 32*(l/16) .. +31 (16 bytes); with
 // fp8 A, lane l holds row l%16, bytes 0-15 at K = 16*(l/16) + i and bytes
 // 16-31 at K = 64 + 16*(l/16) + i; the E8M0 scale supplied by lane 16*b + r
-// applies to row (column) r and K block b.  Within a K chunk of S*128 the
-// MFMA's four K blocks are mapped onto actual blocks S*b + s at step s, so
-// that every lane reads S consecutive weight blocks (16*S contiguous bytes)
-// and S consecutive scale bytes.
+// applies to row (column) r and K block b.
 #include "common.h"
 #include "kernels.h"
+
+#include <algorithm>
 
 namespace moe {
 
@@ -36,311 +43,383 @@ int mxfp4_bm() { return 16; }
 
 namespace {
 
+constexpr int MX_PAD = 16;     // LDS row padding (bytes): rows fall on distinct banks
+
 struct MxP {
     const uint16_t *a;           // GU: x [T, H]; DC: h [rows, ldh]
     const uint8_t *c0, *c1;      // codes [E, N, K/2]
     const uint8_t *s0, *s1;      // scales [E, N, K/32]
-    const int32_t *row_src, *offsets;
-    const float *topk_w;
+    const int32_t *row_tok, *offsets;
     uint16_t *out;
     const Tile *tiles;
     const int32_t *ntiles;
     int T, H, E, k, I, ldh, cap;
 };
 
-// E4M3 (OCP, bias 7) encoding of |v| <= 448, round to nearest even.
+// E4M3 (OCP, bias 7) encoding of |v| <= 448, round to nearest even; both the
+// normal and the subnormal candidate are formed and one is selected, so the
+// conversion has no branch.
 __device__ __forceinline__ uint32_t e4m3(float v, float &q)
 {
     const uint32_t sgn = (__float_as_uint(v) >> 24) & 0x80u;
     const float a = fabsf(v);
-    uint32_t code;
-    float mag;
-    if (a >= 0.015625f) {  // normal: 2^-6 and up
-        uint32_t u = __float_as_uint(a);
-        u = (u + 0x7FFFFu + ((u >> 20) & 1u)) & ~0xFFFFFu;
-        const int e8 = (int)(u >> 23) - 127 + 7;
-        code = ((uint32_t)e8 << 3) | ((u >> 20) & 7u);
-        mag = __uint_as_float(u);
-        if (code > 0x7Eu) {  // saturate at 448
-            code = 0x7Eu;
-            mag = 448.0f;
-        }
-    } else {  // subnormal: multiples of 2^-9
-        const float n = rintf(a * 512.0f);
-        code = (uint32_t)n;  // 8 encodes 2^-6, the smallest normal
-        mag = n * (1.0f / 512.0f);
-    }
+    // normal (2^-6 and up): round the fp32 mantissa to 3 bits
+    uint32_t u = __float_as_uint(a);
+    u = (u + 0x7FFFFu + ((u >> 20) & 1u)) & ~0xFFFFFu;
+    uint32_t cn = ((((u >> 23) - 127u + 7u) & 0xFu) << 3) | ((u >> 20) & 7u);
+    float mn = __uint_as_float(u);
+    const bool sat = u > 0x43E00000u;  // above 448
+    cn = sat ? 0x7Eu : cn;
+    mn = sat ? 448.0f : mn;
+    // subnormal: multiples of 2^-9 (8 encodes 2^-6, the smallest normal)
+    const float ns = rintf(a * 512.0f);
+    const bool normal = a >= 0.015625f;
+    const uint32_t code = normal ? cn : (uint32_t)ns;
+    const float mag = normal ? mn : ns * (1.0f / 512.0f);
     q = sgn ? -mag : mag;
     return sgn | code;
 }
 
-// Quantise the tile's activation rows into LDS: hi / lo E4M3 bytes in natural
-// [row][K] order and their E8M0 scales [row][K/32].
-__device__ void stage_activations(const MxP &p, bool gu, int row0, int nrows, int K,
-                                  uint8_t *ahi, uint8_t *alo, uint8_t *shi, uint8_t *slo)
+// Activation staging: the tile's rows are quantised into LDS, one 32-element
+// block per thread and pass, as hi / lo E4M3 bytes [row][K + MX_PAD] and
+// their E8M0 scales [row][K/32].  A block travels packed (16 registers) and
+// is converted 8 elements at a time.
+__device__ __forceinline__ void block_load(uint4 (&raw)[4], const uint16_t *src)
 {
-    const int lane = threadIdx.x;
-    const int nblk = K / 32;
-    const int n_pairs = p.T * p.k;
-    for (int q = lane; q < nrows * nblk; q += 64) {
-        const int r = q / nblk, b = q % nblk;
-        const int pos = row0 + r;
-        const uint16_t *src = gu ? p.a + (int64_t)pair_token(p.row_src[pos], n_pairs, p.k) * p.H
-                                 : p.a + (int64_t)pos * p.ldh;
-        src += b * 32;
-        float v[32];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint4 w = *(const uint4 *)(src + c * 8);
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    for (int c = 0; c < 4; ++c)
+        raw[c] = *(const uint4 *)(src + c * 8);
+}
+
+// Source of staging block q: row q / nblk (index src[row] of the activation
+// matrix), 32 elements at (q % nblk) * 32.
+__device__ __forceinline__ const uint16_t *block_src(const uint16_t *a, const u32v<4> &src,
+                                                    int64_t lda, int nblk, int q)
+{
+    const int r = q / nblk;
+    uint32_t s = src[0];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v[c * 8 + 2 * i] = bf2f((uint16_t)(ww[i] & 0xFFFF));
-                v[c * 8 + 2 * i + 1] = bf2f((uint16_t)(ww[i] >> 16));
-            }
-        }
-        float amax = 0.0f;
+    for (int i = 1; i < 16; ++i)
+        s = r == i ? src[i] : s;
+    return a + (int64_t)s * lda + (q - r * nblk) * 32;
+}
+
+__device__ __forceinline__ void block_quantise(const uint4 (&raw)[4], int r, int b, int K,
+                                               uint8_t *ahi, uint8_t *alo, uint8_t *shi,
+                                               uint8_t *slo)
+{
+    const int nblk = K / 32, ld = K + MX_PAD;
+    // |bf16| maxima: with the sign bit cleared the bit patterns compare as
+    // the magnitudes do
+    uint32_t mx = 0;
 #pragma unroll
-        for (int i = 0; i < 32; ++i)
-            amax = fmaxf(amax, fabsf(v[i]));
-        int e = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 7;
-        if (amax == 0.0f)
-            e = 0;
-        e = max(e, -123);
-        const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
-        uint32_t hi[8], lo[8];
+    for (int c = 0; c < 4; ++c) {
+        const uint32_t w4[4] = {raw[c].x, raw[c].y, raw[c].z, raw[c].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            mx = max(mx, max(w4[i] & 0x7FFFu, (w4[i] >> 16) & 0x7FFFu));
+    }
+    int e = (int)(mx >> 7) - 127 - 7;  // floor(log2 amax) - 7
+    if (mx == 0)
+        e = 0;
+    e = max(e, -123);
+    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
+    uint8_t *dh = ahi + r * ld + b * 32;
+    uint8_t *dl = alo + r * ld + b * 32;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint32_t w4[4] = {raw[c].x, raw[c].y, raw[c].z, raw[c].w};
+        uint32_t hi[2] = {0, 0}, lo[2] = {0, 0};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            hi[i] = 0;
-            lo[i] = 0;
-        }
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
+            const uint16_t h = (uint16_t)(i & 1 ? w4[i / 2] >> 16 : w4[i / 2] & 0xFFFF);
             float qh, ql;
-            const float xs = v[i] * inv;
+            const float xs = bf2f(h) * inv;
             const uint32_t ch = e4m3(xs, qh);
             const uint32_t cl = e4m3((xs - qh) * 16.0f, ql);
             hi[i / 4] |= ch << (8 * (i % 4));
             lo[i / 4] |= cl << (8 * (i % 4));
         }
-        uint4 *dh = (uint4 *)(ahi + r * K + b * 32);
-        uint4 *dl = (uint4 *)(alo + r * K + b * 32);
-        dh[0] = uint4{hi[0], hi[1], hi[2], hi[3]};
-        dh[1] = uint4{hi[4], hi[5], hi[6], hi[7]};
-        dl[0] = uint4{lo[0], lo[1], lo[2], lo[3]};
-        dl[1] = uint4{lo[4], lo[5], lo[6], lo[7]};
-        shi[r * nblk + b] = (uint8_t)(e + 127);
-        slo[r * nblk + b] = (uint8_t)(e - 4 + 127);
+        *(uint2 *)(dh + 8 * c) = uint2{hi[0], hi[1]};
+        *(uint2 *)(dl + 8 * c) = uint2{lo[0], lo[1]};
     }
+    shi[r * nblk + b] = (uint8_t)(e + 127);
+    slo[r * nblk + b] = (uint8_t)(e - 4 + 127);
 }
 
-// One K chunk of S*128 elements starting at kc: S scaled-MFMA steps per
-// weight matrix and activation half.
-template <int S, int NB>
-__device__ __forceinline__ void mx_chunk(const uint8_t *const *wrow, const uint8_t *const *srow,
-                                         const uint8_t *ahi, const uint8_t *alo,
-                                         const uint8_t *shi, const uint8_t *slo, int K, int kc,
-                                         int ar, bool arow_ok, floatx4 *acc)
-{
-    const int lane = threadIdx.x;
-    const int g4 = lane >> 4;
-    // Weights: 16*S contiguous bytes and S scale bytes per lane and matrix.
-    uint4 wc[NB][S];
-    uint32_t ws[NB];
-#pragma unroll
-    for (int m = 0; m < NB; ++m) {
-        const uint8_t *cp = wrow[m] + (kc + 32 * S * g4) / 2;
-#pragma unroll
-        for (int s = 0; s < S; ++s)
-            wc[m][s] = *(const uint4 *)(cp + 16 * s);
-        const uint8_t *sp = srow[m] + kc / 32 + S * g4;
-        if (S == 4)
-            ws[m] = *(const uint32_t *)sp;
-        else if (S == 2)
-            ws[m] = *(const uint16_t *)sp;
-        else
-            ws[m] = *sp;
-    }
-    const int nblk = K / 32;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        // Activation operand for virtual K block pair (g4/2) and (2 + g4/2).
-        const int off = (g4 & 1) * 16;
-        const int k_lo = kc + 32 * (S * (g4 >> 1) + s) + off;
-        const int k_hi = kc + 32 * (S * (2 + (g4 >> 1)) + s) + off;
-        intx8 ah = {0, 0, 0, 0, 0, 0, 0, 0}, al = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (arow_ok) {
-            const uint4 h0 = *(const uint4 *)(ahi + ar * K + k_lo);
-            const uint4 h1 = *(const uint4 *)(ahi + ar * K + k_hi);
-            const uint4 l0 = *(const uint4 *)(alo + ar * K + k_lo);
-            const uint4 l1 = *(const uint4 *)(alo + ar * K + k_hi);
-            ah = intx8{(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w,
-                       (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
-            al = intx8{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w,
-                       (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
-        }
-        const int sblk = kc / 32 + S * g4 + s;
-        const int sa_h = shi[ar * nblk + sblk];
-        const int sa_l = slo[ar * nblk + sblk];
-#pragma unroll
-        for (int m = 0; m < NB; ++m) {
-            const uint4 c = wc[m][s];
-            const intx8 b = {(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
-            const int sb = (int)((ws[m] >> (8 * s)) & 0xFF);
-            acc[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ah, b, acc[m], 0, 4, 0, sa_h,
-                                                                       0, sb);
-            acc[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(al, b, acc[m], 0, 4, 0, sa_l,
-                                                                       0, sb);
-        }
-    }
-}
-
-// Weights of one S=4 chunk (512 K) for the lane: 64 code bytes and 4 scale
-// bytes per matrix.
-template <int NB>
-struct MxChunk {
-    uint4 c[NB][4];
-    uint32_t s[NB];
+// A lane's weights of one K slab of NQ 128-wide steps, for one column block
+// and matrix, from the packed layout: step s is 16 bytes of a contiguous
+// kilobyte per wave, and the lane's scale bytes of the slab are contiguous
+// (loaded AL at a time, AL the largest of 4, 2, 1 dividing NQ).
+template <int NQ>
+struct MxSlice {
+    static constexpr int AL = NQ % 4 == 0 ? 4 : NQ % 2 == 0 ? 2 : 1;
+    uint4 q[NQ];
+    uint32_t sc[(NQ + 3) / 4];
 };
 
-template <int NB>
-__device__ __forceinline__ void mx_load4(MxChunk<NB> &w, const uint8_t *const *wrow,
-                                         const uint8_t *const *srow, int kc)
+template <int NQ>
+__device__ __forceinline__ void slice_load(MxSlice<NQ> &w, const uint8_t *cbase,
+                                           const uint8_t *sbase, int q0, int s_begin, int s_end)
 {
-    const int g4 = threadIdx.x >> 4;
+    using W = MxSlice<NQ>;
 #pragma unroll
-    for (int m = 0; m < NB; ++m) {
-        const uint8_t *cp = wrow[m] + (kc + 128 * g4) / 2;
+    for (int s = 0; s < NQ; ++s)
+        if (s >= s_begin && s < s_end)
+            w.q[s] = *(const uint4 *)(cbase + (size_t)(q0 + s) * 1024);
+    if (s_begin == 0) {  // the scales of the whole slab go with its first part
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-            w.c[m][s] = *(const uint4 *)(cp + 16 * s);
-        w.s[m] = *(const uint32_t *)(srow[m] + kc / 32 + 4 * g4);
-    }
-}
-
-template <int NB>
-__device__ __forceinline__ void mx_compute4(const MxChunk<NB> &w, const uint8_t *ahi,
-                                            const uint8_t *alo, const uint8_t *shi,
-                                            const uint8_t *slo, int K, int kc, int ar,
-                                            bool arow_ok, floatx4 *acc)
-{
-    const int g4 = threadIdx.x >> 4;
-    const int nblk = K / 32;
+        for (int i = 0; i < (NQ + 3) / 4; ++i)
+            w.sc[i] = 0;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const int off = (g4 & 1) * 16;
-        const int k_lo = kc + 32 * (4 * (g4 >> 1) + s) + off;
-        const int k_hi = kc + 32 * (4 * (2 + (g4 >> 1)) + s) + off;
-        intx8 ah = {0, 0, 0, 0, 0, 0, 0, 0}, al = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (arow_ok) {
-            const uint4 h0 = *(const uint4 *)(ahi + ar * K + k_lo);
-            const uint4 h1 = *(const uint4 *)(ahi + ar * K + k_hi);
-            const uint4 l0 = *(const uint4 *)(alo + ar * K + k_lo);
-            const uint4 l1 = *(const uint4 *)(alo + ar * K + k_hi);
-            ah = intx8{(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w,
-                       (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
-            al = intx8{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w,
-                       (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
-        }
-        const int sblk = kc / 32 + 4 * g4 + s;
-        const int sa_h = shi[ar * nblk + sblk];
-        const int sa_l = slo[ar * nblk + sblk];
-#pragma unroll
-        for (int m = 0; m < NB; ++m) {
-            const uint4 c = w.c[m][s];
-            const intx8 b = {(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
-            const int sb = (int)((w.s[m] >> (8 * s)) & 0xFF);
-            acc[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ah, b, acc[m], 0, 4, 0, sa_h,
-                                                                       0, sb);
-            acc[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(al, b, acc[m], 0, 4, 0, sa_l,
-                                                                       0, sb);
+        for (int a = 0; a < NQ / W::AL; ++a) {
+            const int s = a * W::AL;
+            uint32_t v;
+            if (W::AL == 4)
+                v = *(const uint32_t *)(sbase + q0 + s);
+            else if (W::AL == 2)
+                v = *(const uint16_t *)(sbase + q0 + s);
+            else
+                v = sbase[q0 + s];
+            w.sc[s / 4] |= v << (8 * (s % 4));
         }
     }
 }
 
-template <bool GU>
-__global__ __launch_bounds__(64) void expert_mxfp4(MxP p)
+// One 128-wide K step (hi and lo halves) at absolute step q: the activation
+// operand of row ar from LDS (lane group g4: K = 128q + 16*g4 .. +15 and
+// 64 more), its scale for block 4q + g4, and the weights' operands.
+template <int NB, int CPW>
+__device__ __forceinline__ void mx_step(const uint4 (&b)[NB][CPW], const int (&sb)[NB][CPW],
+                                        const uint8_t *ahi, const uint8_t *alo, const uint8_t *shi,
+                                        const uint8_t *slo, int ld, int nblk, int q, int ar,
+                                        floatx4 (&acc)[NB][CPW])
 {
-    constexpr int NB = GU ? 2 : 1;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    if ((int)blockIdx.y >= *p.ntiles)
-        return;
-    const Tile tile = p.tiles[blockIdx.y];
-    const int g = tile.g, row0 = tile.row0;
-    const int nrows = min(16, p.offsets[g + 1] - row0);
-    const int N = GU ? p.I : p.H;
-    const int K = GU ? p.H : p.I;
-    const int n0 = blockIdx.x * 16;
-    if (n0 >= N)
-        return;
-    const int lane = threadIdx.x;
-    const int n_pairs = p.T * p.k;
-
-    uint8_t *ahi = smem;
-    uint8_t *alo = ahi + p.cap * K;
-    uint8_t *shi = alo + p.cap * K;
-    uint8_t *slo = shi + p.cap * (K / 32);
-
-    const int64_t cstride = (int64_t)N * (K / 2), sstride = (int64_t)N * (K / 32);
-    const int n = n0 + (lane & 15);
-    const uint8_t *wrow[NB], *srow[NB];
-    wrow[0] = p.c0 + g * cstride + (int64_t)n * (K / 2);
-    srow[0] = p.s0 + g * sstride + (int64_t)n * (K / 32);
-    if (GU) {
-        wrow[NB - 1] = p.c1 + g * cstride + (int64_t)n * (K / 2);
-        srow[NB - 1] = p.s1 + g * sstride + (int64_t)n * (K / 32);
-    }
-    // The first two 512-wide weight chunks go out before the activations are
-    // quantised, so their HBM latency overlaps that work.
-    const int nfull = K / 512;
-    MxChunk<NB> wa, wb;
-    if (nfull > 0) {
-        mx_load4<NB>(wa, wrow, srow, 0);
-        mx_load4<NB>(wb, wrow, srow, min(1, nfull - 1) * 512);
-    }
-    stage_activations(p, GU, row0, nrows, K, ahi, alo, shi, slo);
-    __syncthreads();
-
-    const int r = lane & 15;
-    const bool rok = r < nrows;
-    const int ar = rok ? r : 0;
-
-    floatx4 acc[NB];
+    const int g4 = threadIdx.x >> 4 & 3;
+    const int k_lo = 128 * q + 16 * g4;
+    const uint4 h0 = *(const uint4 *)(ahi + ar * ld + k_lo);
+    const uint4 h1 = *(const uint4 *)(ahi + ar * ld + k_lo + 64);
+    const uint4 l0 = *(const uint4 *)(alo + ar * ld + k_lo);
+    const uint4 l1 = *(const uint4 *)(alo + ar * ld + k_lo + 64);
+    const intx8 ah = {(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w,
+                      (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
+    const intx8 al = {(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w,
+                      (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
+    const int sa_h = shi[ar * nblk + 4 * q + g4];
+    const int sa_l = slo[ar * nblk + 4 * q + g4];
 #pragma unroll
     for (int m = 0; m < NB; ++m)
-        acc[m] = floatx4{0, 0, 0, 0};
-    // Two-chunk register pipeline over the 512-wide chunks (the last reloads
-    // are re-reads of the final chunk, never out of bounds).
-    for (int c = 0; c < nfull; c += 2) {
-        mx_compute4<NB>(wa, ahi, alo, shi, slo, K, c * 512, ar, rok, acc);
-        mx_load4<NB>(wa, wrow, srow, min(c + 2, nfull - 1) * 512);
-        if (c + 1 < nfull) {
-            mx_compute4<NB>(wb, ahi, alo, shi, slo, K, (c + 1) * 512, ar, rok, acc);
-            mx_load4<NB>(wb, wrow, srow, min(c + 3, nfull - 1) * 512);
+#pragma unroll
+        for (int cb = 0; cb < CPW; ++cb) {
+            const intx8 bb = {(int)b[m][cb].x, (int)b[m][cb].y, (int)b[m][cb].z,
+                              (int)b[m][cb].w, 0, 0, 0, 0};
+            acc[m][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                ah, bb, acc[m][cb], 0, 4, 0, sa_h, 0, sb[m][cb]);
+            acc[m][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                al, bb, acc[m][cb], 0, 4, 0, sa_l, 0, sb[m][cb]);
+        }
+}
+
+// The tile list, its length and the group offsets come in as read-only
+// kernel arguments: uniform scalar loads, the first two issued together, so
+// a workgroup starts its weight stream one memory latency after it starts.
+template <bool GU, int CPW, int NW, int NQ>
+__global__ __launch_bounds__(64 * NW, 2) void expert_mxfp4(MxP p, const int32_t *__restrict__ ntiles,
+                                                           const Tile *__restrict__ tiles,
+                                                           const int32_t *__restrict__ offsets,
+                                                           const int32_t *__restrict__ row_tok)
+{
+    constexpr int NB = GU ? 2 : 1;
+    using W = MxSlice<NQ>;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int nt = *ntiles;
+    const Tile tile = tiles[blockIdx.y];  // within the list's capacity
+    // both loads feed the test (no short circuit), so they are issued together
+    if (((int)blockIdx.y >= nt) | (tile.g < 0))
+        return;
+    const int g = tile.g, row0 = tile.row0;
+    const int N = GU ? p.I : p.H;
+    const int K = GU ? p.H : p.I;  // a multiple of NQ * 128
+    const int Q = K / 128;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int ld = K + MX_PAD;
+
+    uint8_t *ahi = smem;
+    uint8_t *alo = ahi + p.cap * ld;
+    uint8_t *shi = alo + p.cap * ld;
+    uint8_t *slo = shi + p.cap * (K / 32);
+
+    // This wave's CPW 16-row blocks of each matrix in the packed layout.
+    const uint8_t *cbase[NB][CPW], *sbase[NB][CPW];
+#pragma unroll
+    for (int cb = 0; cb < CPW; ++cb) {
+        const int64_t blk = (int64_t)g * (N / 16) + (blockIdx.x * NW + wave) * CPW + cb;
+        cbase[0][cb] = p.c0 + blk * Q * 1024 + 16 * lane;
+        sbase[0][cb] = p.s0 + (blk * 64 + lane) * Q;
+        if (GU) {
+            cbase[NB - 1][cb] = p.c1 + blk * Q * 1024 + 16 * lane;
+            sbase[NB - 1][cb] = p.s1 + (blk * 64 + lane) * Q;
         }
     }
-    int kc = nfull * 512;
-    if (kc + 256 <= K) {
-        mx_chunk<2, NB>(wrow, srow, ahi, alo, shi, slo, K, kc, ar, rok, acc);
-        kc += 256;
+
+    floatx4 acc[NB][CPW];
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int cb = 0; cb < CPW; ++cb)
+            acc[m][cb] = floatx4{0, 0, 0, 0};
+
+    // The tile's rows (scalar loads): their count and, for gate+up, the token
+    // of each, which locates its activation row.
+    const int nrows = min(16, offsets[g + 1] - row0);
+    const int last = p.T * p.k - 1;  // last grouped row
+    u32v<4> src;  // 16 row indices, held as one vector value (registers)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        src[r] = (uint32_t)(GU ? row_tok[min(row0 + r, last)] : min(row0 + r, last));
+    const int nblk = K / 32;
+    const int nq = nrows * nblk;  // activation blocks to stage
+    const int64_t lda = GU ? p.H : p.ldh;
+
+    // Slab 0: the first half of the weights, then the first pass of
+    // activation blocks, then the second half; the activations, queued ahead
+    // of the second half, arrive while the weights still stream in.  The
+    // scheduling barriers keep that order.
+    W w[NB][CPW];
+    constexpr int H1 = NQ / 2;
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int cb = 0; cb < CPW; ++cb)
+            slice_load<NQ>(w[m][cb], cbase[m][cb], sbase[m][cb], 0, 0, H1);
+    __builtin_amdgcn_sched_barrier(0);
+    const int tid = threadIdx.x;
+    uint4 raw[4];
+    block_load(raw, block_src(p.a, src, lda, nblk, tid < nq ? tid : 0));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int cb = 0; cb < CPW; ++cb)
+            slice_load<NQ>(w[m][cb], cbase[m][cb], sbase[m][cb], 0, H1, NQ);
+    if (tid < nq)
+        block_quantise(raw, tid / nblk, tid % nblk, K, ahi, alo, shi, slo);
+    for (int q = tid + 64 * NW; q < nq; q += 64 * NW) {  // tiles of many rows
+        block_load(raw, block_src(p.a, src, lda, nblk, q));
+        block_quantise(raw, q / nblk, q % nblk, K, ahi, alo, shi, slo);
     }
-    if (kc + 128 <= K)
-        mx_chunk<1, NB>(wrow, srow, ahi, alo, shi, slo, K, kc, ar, rok, acc);
+    __syncthreads();
+    const int ar = (lane & 15) < nrows ? (lane & 15) : 0;  // rows past the tile repeat row 0
+
+    for (int q0 = 0; q0 < Q; q0 += NQ) {
+        if (q0 > 0) {
+#pragma unroll
+            for (int m = 0; m < NB; ++m)
+#pragma unroll
+                for (int cb = 0; cb < CPW; ++cb)
+                    slice_load<NQ>(w[m][cb], cbase[m][cb], sbase[m][cb], q0, 0, NQ);
+        }
+#pragma unroll
+        for (int s = 0; s < NQ; ++s) {
+            uint4 b[NB][CPW];
+            int sb[NB][CPW];
+#pragma unroll
+            for (int m = 0; m < NB; ++m)
+#pragma unroll
+                for (int cb = 0; cb < CPW; ++cb) {
+                    b[m][cb] = w[m][cb].q[s];
+                    sb[m][cb] = (int)(w[m][cb].sc[s / 4] >> (8 * (s % 4)) & 0xFF);
+                }
+            mx_step<NB, CPW>(b, sb, ahi, alo, shi, slo, ld, nblk, q0 + s, ar, acc);
+        }
+    }
 
     // Epilogue: C[4*(l/16) + i][l%16].
+    const int nw0 = (blockIdx.x * NW + wave) * 16 * CPW + (lane & 15);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int m = (lane >> 4) * 4 + i;
         if (m >= nrows)
             continue;
-        const int pos = row0 + m;
-        if (GU) {
-            const float hv = silu(acc[0][i]) * acc[NB - 1][i];
-            p.out[(int64_t)pos * p.ldh + n] = f2bf(hv);
-        } else {
-            p.out[(int64_t)pos * p.H + n] = f2bf(acc[0][i]);
+        const int64_t pos = row0 + m;
+#pragma unroll
+        for (int cb = 0; cb < CPW; ++cb) {
+            const int n = nw0 + 16 * cb;
+            if (GU)
+                p.out[pos * p.ldh + n] = f2bf(silu(acc[0][cb][i]) * acc[NB - 1][cb][i]);
+            else
+                p.out[pos * p.H + n] = f2bf(acc[0][cb][i]);
         }
     }
+}
+
+// Repacking from the OCP row-major form: one thread per 16 code bytes, and
+// one per scale byte.
+__global__ void pack_codes(const uint8_t *__restrict__ in, uint8_t *__restrict__ out, int E, int N,
+                           int K)
+{
+    const int Q = K / 128;
+    const int64_t total = (int64_t)E * N * Q * 4;  // 16-byte chunks
+    for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < total;
+         o += (int64_t)gridDim.x * blockDim.x) {
+        const int l = (int)(o & 63);
+        const int64_t bq = o >> 6;  // (e*N/16 + nb) * Q + q
+        const int q = (int)(bq % Q);
+        const int64_t eb = bq / Q;  // e * N/16 + nb
+        const int64_t row = eb * 16 + (l & 15);  // e * N + n
+        const uint8_t *src = in + row * (K / 2) + (128 * q + 32 * (l >> 4)) / 2;
+        *(uint4 *)(out + o * 16) = *(const uint4 *)src;
+    }
+}
+
+__global__ void pack_scales(const uint8_t *__restrict__ in, uint8_t *__restrict__ out, int E, int N,
+                            int K)
+{
+    const int Q = K / 128;
+    const int64_t total = (int64_t)E * N * Q * 4;  // one byte per (row block, lane, step)
+    for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < total;
+         o += (int64_t)gridDim.x * blockDim.x) {
+        const int q = (int)(o % Q);
+        const int64_t bl = o / Q;  // (e*N/16 + nb) * 64 + l
+        const int l = (int)(bl & 63);
+        const int64_t row = (bl >> 6) * 16 + (l & 15);
+        out[o] = in[row * (K / 32) + 4 * q + (l >> 4)];
+    }
+}
+
+template <bool GU, int CPW, int NW, int NQ>
+void launch(const MxP &p, int N, int K, int tiles, hipStream_t st)
+{
+    const size_t lds = (size_t)p.cap * (2 * (K + MX_PAD) + 2 * (K / 32));
+    static bool attr = false;
+    if (!attr) {
+        (void)hipFuncSetAttribute((const void *)expert_mxfp4<GU, CPW, NW, NQ>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        attr = true;
+    }
+    expert_mxfp4<GU, CPW, NW, NQ>
+        <<<dim3(N / (16 * CPW * NW), tiles), 64 * NW, lds, st>>>(p, p.ntiles, p.tiles, p.offsets,
+                                                                   p.row_tok);
+}
+
+// Slab width (in 128-wide K steps): the largest of 16, 8, 6, 4, 2, 1 that
+// divides K / 128.
+template <bool GU, int CPW, int NW>
+void launch_k(const MxP &p, int N, int K, int tiles, hipStream_t st)
+{
+    const int q = K / 128;
+    if (q % 16 == 0)
+        launch<GU, CPW, NW, 16>(p, N, K, tiles, st);
+    else if (q % 8 == 0)
+        launch<GU, CPW, NW, 8>(p, N, K, tiles, st);
+    else if (q % 6 == 0)
+        launch<GU, CPW, NW, 6>(p, N, K, tiles, st);
+    else if (q % 4 == 0)
+        launch<GU, CPW, NW, 4>(p, N, K, tiles, st);
+    else if (q % 2 == 0)
+        launch<GU, CPW, NW, 2>(p, N, K, tiles, st);
+    else
+        launch<GU, CPW, NW, 1>(p, N, K, tiles, st);
 }
 
 template <bool GU>
@@ -352,9 +431,8 @@ void run(const ExpertArgs &a, hipStream_t st)
     p.c1 = (const uint8_t *)(GU ? a.w_up : nullptr);
     p.s0 = GU ? a.s_gate : a.s_down;
     p.s1 = GU ? a.s_up : nullptr;
-    p.row_src = a.row_src;
+    p.row_tok = a.row_tok;
     p.offsets = a.offsets;
-    p.topk_w = a.topk_w;
     p.out = (uint16_t *)(GU ? a.h : a.stage);
     p.tiles = GU ? a.tiles_gu : a.tiles_dc;
     p.ntiles = GU ? a.ntiles_gu : a.ntiles_dc;
@@ -367,18 +445,27 @@ void run(const ExpertArgs &a, hipStream_t st)
     p.cap = a.T < 16 ? a.T : 16;
     const int K = GU ? a.H : a.I;
     const int N = GU ? a.I : a.H;
-    const size_t lds = (size_t)p.cap * (2 * K + 2 * (K / 32));
-    dim3 grid(N / 16, GU ? a.max_tiles_gu : a.max_tiles_dc);
-    if (grid.y == 0)
+    const int tiles = GU ? a.max_tiles_gu : a.max_tiles_dc;
+    if (tiles == 0)
         return;
-    if (lds > 64 * 1024 &&
-        hipFuncSetAttribute((const void *)expert_mxfp4<GU>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-        return;  // the launch below then reports the error
-    expert_mxfp4<GU><<<grid, 64, lds, st>>>(p);
+    // N is a multiple of 128 (checked at the boundary).  Gate+up: 16 columns
+    // of both matrices per wave; down: 32 columns per wave.
+    if (GU)
+        launch_k<true, 1, 4>(p, N, K, tiles, st);
+    else
+        launch_k<false, 2, 4>(p, N, K, tiles, st);
 }
 
 }  // namespace
+
+void launch_pack_mxfp4(int E, int N, int K, const uint8_t *codes, const uint8_t *scales,
+                       uint8_t *codes_out, uint8_t *scales_out, hipStream_t st)
+{
+    const int64_t chunks = (int64_t)E * N * (K / 128) * 4;
+    const unsigned grid = (unsigned)std::min<int64_t>((chunks + 255) / 256, 65536);
+    pack_codes<<<grid, 256, 0, st>>>(codes, codes_out, E, N, K);
+    pack_scales<<<grid, 256, 0, st>>>(scales, scales_out, E, N, K);
+}
 
 void launch_gate_up_mxfp4(const ExpertArgs &a, hipStream_t st) { run<true>(a, st); }
 void launch_down_mxfp4(const ExpertArgs &a, hipStream_t st) { run<false>(a, st); }

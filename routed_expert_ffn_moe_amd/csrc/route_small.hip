@@ -66,6 +66,7 @@ __global__ __launch_bounds__(256) void router_small(const uint16_t *__restrict__
     }
 }
 
+template <int PER>
 __global__ __launch_bounds__(1024) void route_small(
     const float *__restrict__ logits, int32_t *__restrict__ idx, float *__restrict__ w, int T,
     int E, int k, int shared, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
@@ -76,57 +77,46 @@ __global__ __launch_bounds__(1024) void route_small(
 {
     __shared__ int s_idx[256];
     __shared__ int s_cnt[1025], s_off[1025], s_ta[1025], s_tb[1025];
-    __shared__ int s_warp[3][16];
+    __shared__ int s_warp[16];
+    __shared__ TopkLds s_topk[16];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int P = T * k;
     const int G = E + (shared ? 1 : 0);
 
     // 1. top-k and weights, one wave per token
+    for (int g = tid; g < G; g += 1024)
+        s_cnt[g] = g < E ? 0 : T;
     for (int t = wv; t < T; t += 16)
-        wave_topk(logits + (int64_t)t * E, E, k, idx + (int64_t)t * k, w + (int64_t)t * k,
-                  s_idx + t * k);
+        wave_topk<PER>(logits + (int64_t)t * E, E, k, idx + (int64_t)t * k, w + (int64_t)t * k,
+                       s_idx + t * k, s_topk + wv);
     __syncthreads();
 
-    // 2. pairs per group
-    for (int g = tid; g < G; g += 1024) {
-        int c = 0;
-        if (g < E) {
-            for (int q = 0; q < P; ++q)
-                c += s_idx[q] == g;
-        } else {
-            c = T;
-        }
-        s_cnt[g] = c;
-    }
+    // 2. pairs per group (integer counts: the order of the additions is immaterial)
+    if (tid < P)
+        atomicAdd(&s_cnt[s_idx[tid]], 1);
     __syncthreads();
 
-    // 3. exclusive prefix sums of rows and of the tiles of each list
+    // 3. exclusive prefix sums of the rows and of the tiles of both lists, in
+    // one scan of packed fields (rows < 2^11, tiles < 2^10: at most 272 rows)
     const int c = tid < G ? s_cnt[tid] : 0;
     const int va = tid < G ? (c + bm_a - 1) / bm_a : 0;
     const int vb = tid < G ? (c + bm_b - 1) / bm_b : 0;
-    int ic = c, ia = va, ib = vb;
+    const int v = c | (va << 11) | (vb << 21);
+    int iv = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const int tc = __shfl_up(ic, off), ta = __shfl_up(ia, off), tb = __shfl_up(ib, off);
-        if (lane >= off) {
-            ic += tc;
-            ia += ta;
-            ib += tb;
-        }
+        const int t = __shfl_up(iv, off);
+        if (lane >= off)
+            iv += t;
     }
-    if (lane == 63) {
-        s_warp[0][wv] = ic;
-        s_warp[1][wv] = ia;
-        s_warp[2][wv] = ib;
-    }
+    if (lane == 63)
+        s_warp[wv] = iv;
     __syncthreads();
-    int pc = 0, pa = 0, pb = 0;
-    for (int q = 0; q < wv; ++q) {
-        pc += s_warp[0][q];
-        pa += s_warp[1][q];
-        pb += s_warp[2][q];
-    }
-    const int exc = pc + ic - c, exa = pa + ia - va, exb = pb + ib - vb;
+    int pv = 0;
+    for (int q = 0; q < wv; ++q)
+        pv += s_warp[q];
+    const int ex = pv + iv - v;
+    const int exc = ex & 0x7FF, exa = (ex >> 11) & 0x3FF, exb = (ex >> 21) & 0x3FF;
     if (tid < G) {
         counts[tid] = c;
         offsets[tid] = exc;
@@ -193,12 +183,25 @@ void launch_router_small(const RouterArgs &r, hipStream_t st)
         launch_router_logits(r, st);
 }
 
+template <int PER>
+static void route_small_per(const RouterArgs &r, const PermuteArgs &a, hipStream_t st)
+{
+    route_small<PER><<<1, 1024, 0, st>>>(r.logits, r.idx, r.w, r.T, r.E, r.k, a.shared, a.counts,
+                                         a.offsets, a.row_src, a.row_tok, a.row_of, a.tiles_a,
+                                         a.ntiles_a, a.tiles_b, a.ntiles_b, a.bm_a, a.bm_b,
+                                         a.items_a, a.ntn_a, a.wrows_a, a.items_b, a.ntn_b,
+                                         a.wrows_b);
+}
+
 void launch_route_small(const RouterArgs &r, const PermuteArgs &a, hipStream_t st)
 {
-    route_small<<<1, 1024, 0, st>>>(r.logits, r.idx, r.w, r.T, r.E, r.k, a.shared, a.counts,
-                                    a.offsets, a.row_src, a.row_tok, a.row_of, a.tiles_a,
-                                    a.ntiles_a, a.tiles_b, a.ntiles_b, a.bm_a, a.bm_b, a.items_a,
-                                    a.ntn_a, a.wrows_a, a.items_b, a.ntn_b, a.wrows_b);
+    switch (topk_per(r.E)) {
+    case 1: route_small_per<1>(r, a, st); break;
+    case 2: route_small_per<2>(r, a, st); break;
+    case 4: route_small_per<4>(r, a, st); break;
+    case 8: route_small_per<8>(r, a, st); break;
+    default: route_small_per<16>(r, a, st); break;
+    }
 }
 
 }  // namespace moe

@@ -176,14 +176,18 @@ __global__ __launch_bounds__(256) void router_logits_f32(
 }
 
 // Top-k and weights: one wave per token (see wave_topk).
+template <int PER>
 __global__ __launch_bounds__(256) void router_topk(
     const float *__restrict__ logits, int32_t *__restrict__ idx, float *__restrict__ w,
     int T, int E, int k)
 {
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    __shared__ TopkLds sh[4];
+    const int wv = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wv;
     if (t >= T)
         return;
-    wave_topk(logits + (int64_t)t * E, E, k, idx + (int64_t)t * k, w + (int64_t)t * k, nullptr);
+    wave_topk<PER>(logits + (int64_t)t * E, E, k, idx + (int64_t)t * k, w + (int64_t)t * k,
+                   nullptr, sh + wv);
 }
 
 void launch_router_logits(const RouterArgs &a, hipStream_t st)
@@ -223,7 +227,14 @@ void launch_router(const RouterArgs &a, hipStream_t st)
     if (a.T == 0)
         return;
     launch_router_logits(a, st);
-    router_topk<<<(a.T + 3) / 4, 256, 0, st>>>(a.logits, a.idx, a.w, a.T, a.E, a.k);
+    const unsigned nb = (unsigned)((a.T + 3) / 4);
+    switch (topk_per(a.E)) {
+    case 1: router_topk<1><<<nb, 256, 0, st>>>(a.logits, a.idx, a.w, a.T, a.E, a.k); break;
+    case 2: router_topk<2><<<nb, 256, 0, st>>>(a.logits, a.idx, a.w, a.T, a.E, a.k); break;
+    case 4: router_topk<4><<<nb, 256, 0, st>>>(a.logits, a.idx, a.w, a.T, a.E, a.k); break;
+    case 8: router_topk<8><<<nb, 256, 0, st>>>(a.logits, a.idx, a.w, a.T, a.E, a.k); break;
+    default: router_topk<16><<<nb, 256, 0, st>>>(a.logits, a.idx, a.w, a.T, a.E, a.k); break;
+    }
 }
 
 }  // namespace moe

@@ -66,9 +66,14 @@ class GpuLayer:
         self.c, self.lay, self.dev = c, lay, dev
         self.router_w = act_torch(lay.router_w, c["act"], dev)
         self.router_bias = None if lay.router_bias is None else torch.from_numpy(lay.router_bias).to(dev)
-        self.weights = moe.make_weights(self.router_w, lay.w_gate, lay.w_up, lay.w_down,
-                                        router_bias=self.router_bias, s_gate=lay.s_gate,
-                                        s_up=lay.s_up, s_down=lay.s_down, sh_gate=lay.sh_gate,
+        wg, wu, wd = lay.w_gate, lay.w_up, lay.w_down
+        sg, su, sd = lay.s_gate, lay.s_up, lay.s_down
+        if c["w"] == "mxfp4":  # the layout the kernels read
+            (wg, sg), (wu, su), (wd, sd) = (moe.pack_mxfp4(wg, sg), moe.pack_mxfp4(wu, su),
+                                            moe.pack_mxfp4(wd, sd))
+        self.weights = moe.make_weights(self.router_w, wg, wu, wd,
+                                        router_bias=self.router_bias, s_gate=sg,
+                                        s_up=su, s_down=sd, sh_gate=lay.sh_gate,
                                         sh_up=lay.sh_up, sh_down=lay.sh_down)
 
     def shape(self, T, chunk_T=0):

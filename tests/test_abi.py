@@ -132,3 +132,18 @@ def test_route_rejects_chunking():
 
 def test_zero_tokens_returns_ok_without_touching_buffers():
     assert call(shape(T=0), x=0, y=0, idx=0, ws=0) == moe.MOE_OK
+
+
+@pytest.mark.parametrize("E,N,K,ptrs", [
+    (0, 32, 256, (16, 32, 48, 64)),           # no experts
+    (2, 24, 256, (16, 32, 48, 64)),           # N not a multiple of 16
+    (2, 32, 200, (16, 32, 48, 64)),           # K not a multiple of 128
+    (2, 32, 256, (0, 32, 48, 64)),            # NULL codes
+    (2, 32, 256, (16, 33, 48, 64)),           # misaligned scales
+    (2, 32, 256, (1 << 20, 2 << 20, 1 << 20, 3 << 20)),  # codes_out aliases codes
+])
+def test_pack_mxfp4_rejects_bad_arguments(E, N, K, ptrs):
+    lib = moe.load()
+    rc = lib.moe_pack_mxfp4(E, N, K, *[ctypes.c_void_p(p) for p in ptrs], None)
+    assert rc == moe.MOE_EINVAL
+    assert "moe_pack_mxfp4" in moe.moe_last_error()

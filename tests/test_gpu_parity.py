@@ -195,3 +195,30 @@ def test_graph_replay_matches_eager(name):
         y_e, i_e, w_e = g.forward(xs[r])
         assert torch.equal(idx, i_e) and torch.equal(w, w_e)
         assert torch.equal(y, y_e)
+
+
+def test_pack_mxfp4_layout():
+    """The packed MXFP4 layout, byte for byte, against its definition in the
+    header: codes [E][N/16][K/128][lane][16 B], scales [E][N/16][lane][K/128],
+    lane = r + 16*b for row 16*nb + r and K group 128*s + 32*b."""
+    E, N, K = 3, 48, 768
+    g = torch.Generator().manual_seed(5)
+    codes = torch.randint(0, 256, (E, N, K // 2), generator=g, dtype=torch.uint8)
+    scales = torch.randint(0, 256, (E, N, K // 32), generator=g, dtype=torch.uint8)
+    pc, ps = moe.pack_mxfp4(codes.cuda(), scales.cuda())
+    torch.cuda.synchronize()
+    c, s = codes.numpy(), scales.numpy()
+    Q = K // 128
+    want_c = np.empty((E, N // 16, Q, 64, 16), np.uint8)
+    want_s = np.empty((E, N // 16, 64, Q), np.uint8)
+    for e in range(E):
+        for nb in range(N // 16):
+            for lane in range(64):
+                r, b = lane % 16, lane // 16
+                n = 16 * nb + r
+                for q in range(Q):
+                    k0 = 128 * q + 32 * b
+                    want_c[e, nb, q, lane] = c[e, n, k0 // 2:k0 // 2 + 16]
+                    want_s[e, nb, lane, q] = s[e, n, k0 // 32]
+    assert np.array_equal(pc.cpu().numpy().reshape(-1), want_c.reshape(-1))
+    assert np.array_equal(ps.cpu().numpy().reshape(-1), want_s.reshape(-1))
