@@ -30,8 +30,10 @@ namespace moe {
 
 namespace {
 
-constexpr int SKC = 128;      // K elements of one staged token chunk
-constexpr int SLD = SKC + 8;  // padded LDS row (bf16), 272 bytes
+// A staged token chunk is SKC (128 or 256) K elements wide; its LDS rows are
+// padded by 8 elements, so the 16 rows a fragment read touches fall on
+// distinct banks.
+constexpr int sld_of(int skc) { return skc + 8; }
 // Weight rows per work item and matrix: 4 waves x 32 (gate+up, two
 // matrices) or 4 waves x 64 (down, one matrix).
 constexpr int wrows_of(bool gu) { return gu ? 128 : 256; }
@@ -76,12 +78,12 @@ __device__ __forceinline__ Item item_at(const int4 *__restrict__ items, int wi)
 }
 
 // Element offsets (into x or h) of the token rows this thread stages.
-template <int ACH, bool GU>
+template <int ACH, bool GU, int SKC>
 __device__ __forceinline__ void item_rows(const StreamP &p, const Item &it, int tid, int (&aro)[ACH])
 {
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
-        const int pos = it.row0 + min((tid + 256 * i) >> 4, it.nrows - 1);
+        const int pos = it.row0 + min((tid + 256 * i) / (SKC / 8), it.nrows - 1);
         aro[i] = GU ? p.row_tok[pos] * p.H : pos * p.ldh;
     }
 }
@@ -100,37 +102,57 @@ __device__ __forceinline__ void rows_load(u32v<ACH> &r, const uint16_t *x, const
     }
 }
 
-// One 32-wide K step (step s4 of a token chunk) over the first NMB token
-// blocks: consume the weight fragments of ring slot `slot` and refill it from
-// wl + wk (the step SD steps ahead), then run the token blocks.
-template <int NMB, int MB, int NB, int CB, int SD>
-__device__ __forceinline__ void kstep(const uint16_t *As, int slot, int s4, int l16, int lg,
-                                      uint4 (&bq)[SD][NB][CB], const uint16_t *const (&wl)[NB],
-                                      int wk, const int (&woff)[CB], floatx4 (&acc)[NB][CB][MB])
+// Token fragments of K step s4 of the staged chunk: lane (l16, lg) holds
+// token row mb*16 + l16, K = 32*s4 + 8*lg .. +7.
+template <int NMB, int SLD>
+__device__ __forceinline__ void frag_load(bf16x8 (&tf)[NMB], const uint16_t *As, int s4, int l16,
+                                          int lg)
 {
-    // Take the weight fragments of this step and refill their ring slot.
-    bf16x8 wf[NB][CB];
 #pragma unroll
-    for (int m = 0; m < NB; ++m)
+    for (int mb = 0; mb < NMB; ++mb)
+        tf[mb] = as_bf16x8(*(const uint4 *)(As + (mb * 16 + l16) * SLD + s4 * 32 + lg * 8));
+}
+
+// The SKC/32 K steps of a staged token chunk.  Step s consumes the weight
+// fragments of ring slot (slot0 + s) % SD and refills it from the step SD
+// ahead (chunk wl[(s + SD) / SPC], step (s + SD) % SPC); the token fragments
+// of step s + 1 are read from LDS before the MFMAs of step s run, so LDS
+// latency hides behind them.
+template <int MB, int NB, int CB, int SD, int SKC>
+__device__ __forceinline__ void kchunk(const uint16_t *As, int slot0, int l16, int lg,
+                                       uint4 (&bq)[SD][NB][CB],
+                                       const uint16_t *const (&wl)[3][NB],
+                                       const int (&woff)[CB], floatx4 (&acc)[NB][CB][MB])
+{
+    constexpr int SPC = SKC / 32, SLD = sld_of(SKC);
+    static_assert((SPC - 1 + SD) / SPC <= 2, "refills reach at most two chunks ahead");
+    bf16x8 tf[2][MB];
+    frag_load<MB, SLD>(tf[0], As, 0, l16, lg);
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            wf[m][cb] = as_bf16x8(bq[slot][m][cb]);
-            bq[slot][m][cb] = *(const uint4 *)(wl[m] + woff[cb] + wk);
-        }
-    // issue the refills here, not later: the wait for this step's token
-    // chunk must not have to wait for them
-    __builtin_amdgcn_sched_barrier(0);
-    // Token block by token block: each LDS fragment feeds NB*CB MFMAs, so
-    // the next block's read overlaps the current block's MFMAs.
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-        const bf16x8 tf =
-            as_bf16x8(*(const uint4 *)(As + (mb * 16 + l16) * SLD + s4 * 32 + lg * 8));
+    for (int st = 0; st < SPC; ++st) {
+        const int slot = (slot0 + st) % SD;
+        bf16x8 wf[NB][CB];
+        const uint16_t *const *w = wl[(st + SD) / SPC];
+        const int wk = ((st + SD) % SPC) * 32;
 #pragma unroll
         for (int m = 0; m < NB; ++m)
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-                acc[m][cb][mb] = mfma16(wf[m][cb], tf, acc[m][cb][mb]);
+            for (int cb = 0; cb < CB; ++cb) {
+                wf[m][cb] = as_bf16x8(bq[slot][m][cb]);
+                bq[slot][m][cb] = *(const uint4 *)(w[m] + woff[cb] + wk);
+            }
+        if (st + 1 < SPC)
+            frag_load<MB, SLD>(tf[(st + 1) & 1], As, st + 1, l16, lg);
+        // issue the refills and the next fragments here, not later: the
+        // waits for this step's operands must not have to wait for them
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int m = 0; m < NB; ++m)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+                    acc[m][cb][mb] = mfma16(wf[m][cb], tf[st & 1][mb], acc[m][cb][mb]);
     }
 }
 
@@ -144,15 +166,17 @@ __device__ __forceinline__ void kstep(const uint16_t *As, int slot, int s4, int 
 // the LDS and L2 latency that one wave's own schedule cannot.
 constexpr int wg_per_cu(int bm) { return bm <= 16 ? 3 : bm <= 64 ? 2 : 1; }
 
-template <int BM, bool GU, int SD>
+template <int BM, bool GU, int SD, int SKC>
 __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
                                                                     const int4 *__restrict__ items)
 {
+    constexpr int SLD = sld_of(SKC), SPC = SKC / 32, RW = SKC / 8;  // 16-byte pieces per row
     constexpr int NB = GU ? 2 : 1;             // weight matrices
     constexpr int CB = GU ? 2 : 4;             // 16-row weight blocks per wave and matrix
     constexpr int MB = BM / 16;                // 16-row token blocks
     constexpr int ACH = BM * (SKC / 8) / 256;  // 16-byte token chunks per thread
-    static_assert(SD == 2 || SD == 4 || SD == 8, "prefetch ring depth in K steps");
+    static_assert(SD == 4 || SD == 8, "prefetch ring depth in K steps");
+    static_assert((2 * SPC) % SD == 0, "ring slots line up with chunk pairs");
     static_assert(ACH >= 1 && ACH * 256 == BM * SKC / 8, "token staging");
     static_assert(CB % 2 == 0 && 4 * CB * 16 == wrows_of(GU), "column blocks go in pairs");
 
@@ -195,7 +219,7 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
     int aoff[ACH];
 #pragma unroll
     for (int i = 0; i < ACH; ++i)
-        aoff[i] = ((tid + 256 * i) >> 4) * SLD + (tid & 15) * 8;
+        aoff[i] = ((tid + 256 * i) / RW) * SLD + (tid % RW) * 8;
 
     // Prologue: first item's weights for chunk 0, its token rows, chunk 0 in LDS.
     Item cur = item_at(items, base + slot);
@@ -213,13 +237,13 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
             for (int cb = 0; cb < CB; ++cb)
                 bq[d][m][cb] = *(const uint4 *)(wc[m] + woff[cb] + d * 32);  // SD <= 8 <= K/32
     int aro[ACH], aro_n[ACH];
-    item_rows<ACH, GU>(p, cur, tid, aro);
-    item_rows<ACH, GU>(p, nxt, tid, aro_n);
+    item_rows<ACH, GU, SKC>(p, cur, tid, aro);
+    item_rows<ACH, GU, SKC>(p, nxt, tid, aro_n);
     u32v<ACH> ra;
-    rows_load<ACH>(ra, p.x, aro, (tid & 15) * 8);
+    rows_load<ACH>(ra, p.x, aro, (tid % RW) * 8);
     chunk_store<ACH>(ra, sA[0], aoff);
     __syncthreads();
-    rows_load<ACH>(ra, p.x, aro, SKC + (tid & 15) * 8);
+    rows_load<ACH>(ra, p.x, aro, SKC + (tid % RW) * 8);
     int buf = 0;
 
     for (int j = 0; j < nitems; ++j) {
@@ -258,12 +282,8 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
                     for (int m = 0; m < NB; ++m)
                         wl[d][m] = (over ? wn[m] : wc[m]) + tk;
                 }
-                // Every row block is computed, also those past the tile's rows:
-                // such tiles are bound by their weight stream, not by the MFMAs.
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4)
-                    kstep<MB, MB, NB, CB, SD>(As, (h * 4 + s4) % SD, s4, l16, lg, bq,
-                                              wl[(s4 + SD) / 4], ((s4 + SD) % 4) * 32, woff, acc);
+                // Every row block is computed, also those past the item's rows.
+                kchunk<MB, NB, CB, SD, SKC>(As, h * SPC, l16, lg, bq, wl, woff, acc);
                 // Token chunk pipeline: ra holds the chunk after this one.
                 chunk_store<ACH>(ra, sA[buf ^ 1], aoff);
                 __syncthreads();
@@ -274,7 +294,7 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
 #pragma unroll
                 for (int i = 0; i < ACH; ++i)
                     rsel[i] = over ? aro_n[i] : aro[i];
-                rows_load<ACH>(ra, p.x, rsel, (c2 - over * nchunks) * SKC + (tid & 15) * 8);
+                rows_load<ACH>(ra, p.x, rsel, (c2 - over * nchunks) * SKC + (tid % RW) * 8);
                 // keep these loads ahead of the next steps' weight loads, so
                 // that waiting for them never waits for the weight stream
                 __builtin_amdgcn_sched_barrier(0);
@@ -323,11 +343,11 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
 #pragma unroll
         for (int i = 0; i < ACH; ++i)
             aro[i] = aro_n[i];
-        item_rows<ACH, GU>(p, nxt, tid, aro_n);
+        item_rows<ACH, GU, SKC>(p, nxt, tid, aro_n);
     }
 }
 
-template <int BM, bool GU, int SD>
+template <int BM, bool GU, int SD, int SKC>
 void run(const ExpertArgs &a, hipStream_t st)
 {
     StreamP p;
@@ -369,13 +389,15 @@ void run(const ExpertArgs &a, hipStream_t st)
     int &occ = per_cu[GU ? 1 : 0];
     if (!occ) {
         int b = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, expert_stream<BM, GU, SD>, 256, 0) != hipSuccess || b < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, expert_stream<BM, GU, SD, SKC>, 256,
+                                                         0) != hipSuccess ||
+            b < 1)
             b = 1;
         occ = b;
     }
     const int64_t per_xcd = (items + 7) / 8;
     const int64_t slots = std::min<int64_t>(per_xcd, (int64_t)(cus / 8) * occ);
-    expert_stream<BM, GU, SD><<<(unsigned)(slots * 8), 256, 0, st>>>(p, p.items);
+    expert_stream<BM, GU, SD, SKC><<<(unsigned)(slots * 8), 256, 0, st>>>(p, p.items);
 }
 
 }  // namespace
@@ -422,31 +444,53 @@ int stream_bm(const ExpertArgs &a)
     return 128;
 }
 
-// Prefetch ring depth in K steps; MOE_STREAM_SD (2, 4 or 8) overrides the
+// Prefetch ring depth in K steps; MOE_STREAM_SD (4 or 8) overrides the
 // default for tuning runs (read once per process).
 static int stream_sd(int bm)
 {
     static const int forced = [] {
         const char *e = getenv("MOE_STREAM_SD");
         const int v = e ? atoi(e) : 0;
-        return (v == 2 || v == 4 || v == 8) ? v : 0;
+        return (v == 4 || v == 8) ? v : 0;
     }();
     if (forced)
         return forced;
     (void)bm;
-    return 4;  // deeper rings spill under the occupancy bounds (see wg_per_cu)
+    return 4;  // deeper rings spill under the occupancy bounds (see wg_per_cu) or gain nothing
+}
+
+// Token chunk width: 256 K for the small row tiles where the chunks still
+// come in pairs, else 128;
+// MOE_STREAM_SKC (128 or 256) overrides it for tuning runs.
+static int stream_skc(int K, int bm)
+{
+    static const int forced = [] {
+        const char *e = getenv("MOE_STREAM_SKC");
+        const int v = e ? atoi(e) : 0;
+        return (v == 128 || v == 256) ? v : 0;
+    }();
+    if (forced == 128 || (forced == 256 && K % 512 == 0))
+        return forced;
+    // the wide chunk's staging registers only fit beside the small row tiles
+    return K % 512 == 0 && bm <= 32 ? 256 : 128;
+}
+
+template <int BM, bool GU, int SKC>
+static void run_skc(const ExpertArgs &a, hipStream_t st)
+{
+    if (stream_sd(BM) == 8)
+        run<BM, GU, 8, SKC>(a, st);
+    else
+        run<BM, GU, 4, SKC>(a, st);
 }
 
 template <int BM, bool GU>
 static void run_sd(const ExpertArgs &a, hipStream_t st)
 {
-    const int sd = stream_sd(BM);
-    if (sd == 2)
-        run<BM, GU, 2>(a, st);
-    else if (sd == 4)
-        run<BM, GU, 4>(a, st);
+    if (stream_skc(GU ? a.H : a.I, BM) == 256)
+        run_skc<BM, GU, 256>(a, st);
     else
-        run<BM, GU, 8>(a, st);
+        run_skc<BM, GU, 128>(a, st);
 }
 
 template <bool GU>
