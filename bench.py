@@ -70,13 +70,14 @@ def roofline(work, stage, ms, dtype):
 
 
 class Workload:
-    def __init__(self, name, wsets=1, dev="cuda"):
+    def __init__(self, name, wsets=1, dev="cuda", keep_rowmajor=False):
         import torch
 
         import moe_inputs as mi
         import routed_expert_ffn_moe_amd as moe
         self.torch, self.moe = torch, moe
         self.name = name
+        self.keep_rowmajor = keep_rowmajor
         self.c = mi.cfg(name)
         c = self.c
         self.layers = [mi.make_layer(c, dev, s) for s in range(wsets)]
@@ -93,13 +94,22 @@ class Workload:
             self._keep += [rw, rb]
             wg, wu, wd = lay.w_gate, lay.w_up, lay.w_down
             sg, su, sd = lay.s_gate, lay.s_up, lay.s_down
-            if c["w"] == "mxfp4":  # one-time repack into the layout the kernels read
+            shg, shu, shd = lay.sh_gate, lay.sh_up, lay.sh_down
+            # one-time repack into the layouts the kernels read (the row-major
+            # copies go, so that the widest layer still fits twice over)
+            if c["w"] == "mxfp4":
                 (wg, sg), (wu, su), (wd, sd) = (moe.pack_mxfp4(wg, sg), moe.pack_mxfp4(wu, su),
                                                 moe.pack_mxfp4(wd, sd))
-                self._keep += [wg, wu, wd, sg, su, sd]
+            elif c["w"] == "bf16":
+                wg, wu, wd = (self._packed(lay, "w_gate"), self._packed(lay, "w_up"),
+                              self._packed(lay, "w_down"))
+            if c["act"] == "bf16" and shg is not None:
+                shg, shu, shd = (self._packed(lay, "sh_gate"), self._packed(lay, "sh_up"),
+                                 self._packed(lay, "sh_down"))
+            self._keep += [wg, wu, wd, sg, su, sd, shg, shu, shd]
             self.weights.append(moe.make_weights(rw, wg, wu, wd, router_bias=rb, s_gate=sg,
-                                                 s_up=su, s_down=sd, sh_gate=lay.sh_gate,
-                                                 sh_up=lay.sh_up, sh_down=lay.sh_down))
+                                                 s_up=su, s_down=sd, sh_gate=shg,
+                                                 sh_up=shu, sh_down=shd))
         self.shape = moe.make_shape(c["T"], c["H"], c["E"], c["top_k"], c["I"], c["I_shared"],
                                     0, c["act"], c["w"])
         nb = moe.moe_workspace_bytes(self.shape)
@@ -157,6 +167,16 @@ class Workload:
             graphs[i % len(graphs)].replay()
         torch.cuda.synchronize()
         return time.perf_counter() - t0
+
+    def _packed(self, lay, name):
+        """Packed copy of one bf16 matrix of `lay`; the row-major original is
+        kept only for the primary workload (the CPU baseline reads it)."""
+        w = getattr(lay, name)
+        out = self.moe.pack_bf16(w)
+        self.torch.cuda.synchronize()
+        if not self.keep_rowmajor:
+            setattr(lay, name, None)
+        return out
 
     def counts(self):
         import numpy as np
@@ -283,7 +303,7 @@ def main():
         torch.cuda.empty_cache()
     out["also"] = also
     if not args.no_cpu_baseline:
-        wl = Workload(args.workload)
+        wl = Workload(args.workload, keep_rowmajor=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

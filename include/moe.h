@@ -33,6 +33,8 @@
  *     [E, N, K/32], one per 32 consecutive K elements ([N, K] = [I, H] for
  *     gate and up, [H, I] for down).
  *   sh_gate, sh_up [I_shared, H], sh_down [H, I_shared]   act_dtype
+ *     BF16 expert matrices (routed and shared) are passed as moe_pack_bf16
+ *     lays them out (below); F32 ones row-major as listed.
  *   topk_idx [T, top_k] int32, topk_w [T, top_k] float
  *
  * Packed MXFP4 (what the kernels read: each wave's weights are whole
@@ -43,6 +45,13 @@
  *   scales [E][N/16][64 lanes][q]: byte s of lane l is the scale of row n
  *          at K = 128*s + 32*b .. +31.
  * The packed matrices have the same sizes as the OCP ones.
+ *
+ * Packed BF16 (what the kernels read: a wave's weight fragment of one MFMA
+ * step is a contiguous kilobyte).  Rows go in groups of 32 (g = n / 32) and
+ * K in steps of 32 (s = k / 32); each (g, s) is two 1 KB blocks c = 0, 1;
+ * lane l = r + 16*b (r = 0..15, b = 0..3) of block c holds the 8 elements
+ * of row n = 32*g + 8*(r/4) + 4*c + r%4 at K = 32*s + 8*b .. +7:
+ *   [E][N/32][K/32][2][64 lanes][8 bf16].
  *
  * Supported combinations: act F32 with w F32; act BF16 with w BF16 or MXFP4.
  * MXFP4 needs H and I multiples of 128, at most 4096, and no shared expert
@@ -131,6 +140,13 @@ int moe_route(const moe_shape_t *shape, const moe_weights_t *w,
  * step when weights are loaded.  MOE_EINVAL on bad sizes or pointers. */
 int moe_pack_mxfp4(int E, int N, int K, const void *codes, const uint8_t *scales,
                    void *codes_out, uint8_t *scales_out, void *stream);
+
+/* Repack E bf16 matrices of N rows and K columns (multiples of 32) from the
+ * row-major form [E, N, K] into the layout moe_forward reads (above); the
+ * same number of bytes out.  Device pointers, 16-byte aligned, not
+ * overlapping; asynchronous on `stream`.  A one-time step when weights are
+ * loaded.  MOE_EINVAL on bad sizes or pointers. */
+int moe_pack_bf16(int E, int N, int K, const void *w, void *w_out, void *stream);
 
 /* Stage timing for measurement (not needed for computing).  While enabled,
  * moe_forward records a pair of HIP events on its stream around each of its

@@ -18,8 +18,8 @@ __all__ = [
     "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_OK", "MOE_EINVAL", "MOE_EWORKSPACE",
     "MOE_EUNSUPPORTED", "MOE_EHIP", "MoeError", "moe_shape_t", "moe_weights_t", "make_shape",
     "make_weights", "moe_workspace_bytes", "moe_forward", "moe_route", "moe_strerror",
-    "moe_last_error", "moe_stage_timing_enable", "moe_stage_timing_read", "moe_pack_mxfp4",
-    "pack_mxfp4", "STAGES",
+    "moe_last_error", "moe_stage_timing_enable", "moe_stage_timing_read", "moe_pack_bf16",
+    "pack_bf16", "moe_pack_mxfp4", "pack_mxfp4", "STAGES",
     "lib_path", "load",
 ]
 
@@ -76,6 +76,8 @@ def load() -> ctypes.CDLL:
         lib.moe_stage_timing_enable.argtypes = [ctypes.c_int]
         lib.moe_stage_timing_read.restype = ctypes.c_int
         lib.moe_stage_timing_read.argtypes = [P, ctypes.c_int, P]
+        lib.moe_pack_bf16.restype = ctypes.c_int
+        lib.moe_pack_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P]
         lib.moe_pack_mxfp4.restype = ctypes.c_int
         lib.moe_pack_mxfp4.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
         _lib = lib
@@ -147,6 +149,20 @@ def moe_route(shape, weights, x, topk_idx, topk_w, counts, offsets, row_src, ws,
     _check(load().moe_route(ctypes.byref(shape), ctypes.byref(weights.c), _ptr(x),
                             _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets),
                             _ptr(row_src), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_pack_bf16(E, N, K, w, w_out, stream=None) -> None:
+    """Repack row-major bf16 matrices [E, N, K] into the layout moe_forward reads."""
+    _check(load().moe_pack_bf16(E, N, K, _ptr(w), _ptr(w_out), _stream(stream)))
+
+
+def pack_bf16(w, stream=None):
+    """Packed copy of a bf16 device tensor [E, N, K] or [N, K]."""
+    import torch
+    E, N, K = (1, *w.shape) if w.dim() == 2 else w.shape
+    out = torch.empty_like(w)
+    moe_pack_bf16(E, N, K, w, out, stream)
+    return out
 
 
 def moe_pack_mxfp4(E, N, K, codes, scales, codes_out, scales_out, stream=None) -> None:

@@ -74,6 +74,16 @@ __device__ __forceinline__ uint4 vget(const u32v<N> &r, int i)
     return uint4{r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]};
 }
 
+// Offset (elements) of the 8 K-consecutive elements (n, k .. k+7) of a bf16
+// matrix [N, K] in the packed layout (k a multiple of 8): rows in groups of
+// 32, K in steps of 32, each (group, step) two kilobyte blocks whose lane
+// r + 16*b holds row 32*g + 8*(r/4) + 4*c + r%4 at K = 32*s + 8*b.
+__device__ __forceinline__ int64_t packed_bf16_off(int n, int k, int K)
+{
+    const int j = n & 31, c = (j & 7) >> 2, r = 4 * (j >> 3) + (j & 3), b = (k & 31) >> 3;
+    return ((((int64_t)(n >> 5) * (K >> 5) + (k >> 5)) * 2 + c) * 64 + r + 16 * b) * 8;
+}
+
 // Tile descriptor written by the permutation: group g (expert, or E for the
 // shared expert) and the first grouped row of the tile.
 struct Tile {

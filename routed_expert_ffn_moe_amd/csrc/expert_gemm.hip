@@ -20,6 +20,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace moe {
 
 namespace {
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(256) void expert_gemm_bf16(GemmP p)
         int rem = c % (BN * BK / 8);
         int r = rem / (BK / 8), c8 = rem % (BK / 8);
         const uint16_t *W = (m == 0) ? W0 : W1;
-        bsrc[i] = W + (int64_t)(n0 + r) * K + c8 * 8;
+        bsrc[i] = W + packed_bf16_off(n0 + r, c8 * 8, K);
         boff[i] = (m * BN + r) * LDK + c8 * 8;
     }
 
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(256) void expert_gemm_bf16(GemmP p)
                 ra[i] = *(const uint4 *)(asrc[i] + k0);
 #pragma unroll
         for (int i = 0; i < BCH; ++i)
-            rb[i] = *(const uint4 *)(bsrc[i] + k0);
+            rb[i] = *(const uint4 *)(bsrc[i] + (int64_t)k0 * 32);  // k0 / 32 steps of 1024
     };
     auto sstore = [&](int buf) {
 #pragma unroll
@@ -434,6 +436,36 @@ void launch_down(const ExpertArgs &a, hipStream_t st)
         launch_stream(a, false, st);
     else
         dispatch<false>(a, st);
+}
+
+namespace {
+
+// Row-major [E, N, K] bf16 into the packed layout: one thread per 16 bytes
+// out (the 8 elements of one lane of one block).
+__global__ void pack_bf16(const uint16_t *__restrict__ in, uint16_t *__restrict__ out, int E, int N,
+                          int K)
+{
+    const int64_t total = (int64_t)E * N * (K / 8);
+    for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < total;
+         o += (int64_t)gridDim.x * blockDim.x) {
+        const int l = (int)(o & 63);
+        const int c = (int)((o >> 6) & 1);
+        const int64_t gs = o >> 7;  // (e * N/32 + g) * K/32 + s
+        const int s = (int)(gs % (K / 32));
+        const int64_t eg = gs / (K / 32);  // e * N/32 + g
+        const int r = l & 15, b = l >> 4;
+        const int64_t row = eg * 32 + 8 * (r >> 2) + 4 * c + (r & 3);  // e * N + n
+        *(uint4 *)(out + o * 8) = *(const uint4 *)(in + row * K + 32 * s + 8 * b);
+    }
+}
+
+}  // namespace
+
+void launch_pack_bf16(int E, int N, int K, const uint16_t *w, uint16_t *out, hipStream_t st)
+{
+    const int64_t chunks = (int64_t)E * N * (K / 8);
+    const unsigned grid = (unsigned)std::min<int64_t>((chunks + 255) / 256, 65536);
+    pack_bf16<<<grid, 256, 0, st>>>(w, out, E, N, K);
 }
 
 void launch_combine(const CombineArgs &a, hipStream_t st)

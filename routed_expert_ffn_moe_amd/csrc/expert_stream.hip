@@ -7,16 +7,19 @@
 // matters ("MoE prefill quantum", Table 9 and the text after it: small chunks
 // read nearly every expert's weights for a few rows each).
 //
-//  * Each wave owns 32 weight rows per matrix (two 16-row MFMA blocks) and
-//    streams them from HBM straight into registers through a prefetch ring of
-//    4 or 8 steps of 32 K: no LDS and no barrier on the weight path, every
-//    weight element read once per tile.
-//  * The tile's token rows (gathered through row_src) are staged in LDS in
-//    double-buffered 128-wide K chunks shared by the 4 waves.
+//  * Each wave owns 32 weight rows per matrix (gate+up: two matrices) or 64
+//    (down) and streams them from HBM straight into registers through a
+//    prefetch ring of 4 or 8 steps of 32 K: no LDS and no barrier on the
+//    weight path, every weight element read once per tile.  The weights are
+//    in the packed layout (moe_pack_bf16): one K step of a 16-row block is a
+//    contiguous kilobyte, so each load instruction of a wave fetches whole
+//    cache lines (row-major rows would give 64 bytes of each of 16 lines).
+//  * The tile's token rows (gathered through row_tok) are staged in LDS in
+//    double-buffered 128- or 256-wide K chunks shared by the 4 waves.
 //  * The MFMA takes the weights as its A operand and the tokens as B; with
-//    the weight rows of the two column blocks interleaved by fours, a lane
-//    ends up with 8 adjacent output columns of one token row and stores them
-//    as one 16-byte word (64 contiguous bytes per row and wave).
+//    the weight rows of the two blocks of a 32-row group interleaved by fours,
+//    a lane ends up with 8 adjacent output columns of one token row and
+//    stores them as one 16-byte word (64 contiguous bytes per row and wave).
 //  * Work items are ordered expert-major (then weight tile, then row tile)
 //    and dealt out XCD by XCD in contiguous runs, so an expert's weight tiles
 //    and token rows are fetched into one XCD's L2 and reused there.
@@ -139,7 +142,7 @@ __device__ __forceinline__ void kchunk(const uint16_t *As, int slot0, int l16, i
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
                 wf[m][cb] = as_bf16x8(bq[slot][m][cb]);
-                bq[slot][m][cb] = *(const uint4 *)(w[m] + woff[cb] + wk);
+                bq[slot][m][cb] = *(const uint4 *)(w[m] + woff[cb] + wk * 32);
             }
         if (st + 1 < SPC)
             frag_load<MB, SLD>(tf[(st + 1) & 1], As, st + 1, l16, lg);
@@ -198,18 +201,20 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
     const int n_pairs = p.T * p.k;
     const int N = GU ? p.I : p.H;
     const int K = GU ? p.H : p.I;
-    const int nchunks = K / SKC;  // even, >= 2
+    const int nchunks = K / SKC;  // even, >= 4
     const int64_t wstride = (int64_t)N * K;
 
-    // Weight rows of this lane: the blocks go in pairs of 32 rows; MFMA row
-    // l16 of block cb is weight row n0 + wave*16*CB + 32*(cb/2) + 8*(l16/4) +
-    // 4*(cb%2) + l16%4, so that after the MFMA the lane with lg = l16/4 holds
-    // 8 consecutive output columns per pair and stores them as one 16-byte word.
+    // Weight fragments of this lane in the packed layout: block cb of the
+    // wave is block (cb & 1) of 32-row group wave * CB / 2 + cb / 2 of the
+    // item's slice, whose MFMA row l16 is weight row 32 * group + 8 * (l16 / 4)
+    // + 4 * (cb % 2) + l16 % 4; so after the MFMA the lane with lg = l16 / 4
+    // holds 8 consecutive output columns per pair of blocks and stores them
+    // as one 16-byte word.  One K step of a block is a contiguous kilobyte
+    // (1024 elements per 32 K: offsets below scale K positions by 32).
     int woff[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
-        woff[cb] = (wave * 16 * CB + 32 * (cb >> 1) + 8 * (l16 >> 2) + 4 * (cb & 1) + (l16 & 3)) * K +
-                   lg * 8;
+        woff[cb] = ((wave * CB / 2 + cb / 2) * (K / 32) * 2 + (cb & 1)) * 512 + lane * 8;
     auto wbase = [&](const Item &it, int m) -> const uint16_t * {
         const bool routed = it.g < p.E;
         const uint16_t *W = m == 0 ? (routed ? p.w0 + (int64_t)it.g * wstride : p.s0)
@@ -235,15 +240,20 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
         for (int m = 0; m < NB; ++m)
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb)
-                bq[d][m][cb] = *(const uint4 *)(wc[m] + woff[cb] + d * 32);  // SD <= 8 <= K/32
+                bq[d][m][cb] = *(const uint4 *)(wc[m] + woff[cb] + d * 1024);  // SD <= 8 <= K/32
     int aro[ACH], aro_n[ACH];
     item_rows<ACH, GU, SKC>(p, cur, tid, aro);
     item_rows<ACH, GU, SKC>(p, nxt, tid, aro_n);
-    u32v<ACH> ra;
-    rows_load<ACH>(ra, p.x, aro, (tid % RW) * 8);
-    chunk_store<ACH>(ra, sA[0], aoff);
+    // Token chunks in flight: TL ahead of the one in LDS (two measured no
+    // faster than one: the weights, not the token rows, set the pace).
+    constexpr int TL = 1;
+    u32v<ACH> rt[TL];
+    rows_load<ACH>(rt[0], p.x, aro, (tid % RW) * 8);
+    chunk_store<ACH>(rt[0], sA[0], aoff);
     __syncthreads();
-    rows_load<ACH>(ra, p.x, aro, SKC + (tid % RW) * 8);
+#pragma unroll
+    for (int t = 0; t < TL; ++t)
+        rows_load<ACH>(rt[t], p.x, aro, (1 + t) * SKC + (tid % RW) * 8);  // 1 + TL <= nchunks
     int buf = 0;
 
     for (int j = 0; j < nitems; ++j) {
@@ -277,18 +287,20 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
                 for (int d = 0; d < 3; ++d) {
                     const int t = cc + d;
                     const int over = t >= nchunks;
-                    const int tk = (t - over * nchunks) * SKC;
+                    const int tk = (t - over * nchunks) * SKC * 32;  // packed: 32 per K
 #pragma unroll
                     for (int m = 0; m < NB; ++m)
                         wl[d][m] = (over ? wn[m] : wc[m]) + tk;
                 }
                 // Every row block is computed, also those past the item's rows.
                 kchunk<MB, NB, CB, SD, SKC>(As, h * SPC, l16, lg, bq, wl, woff, acc);
-                // Token chunk pipeline: ra holds the chunk after this one.
+                // Token chunk pipeline: rt[h % TL] holds the chunk after this
+                // one and is reloaded with the chunk TL + 1 ahead.
+                u32v<ACH> &ra = rt[h % TL];
                 chunk_store<ACH>(ra, sA[buf ^ 1], aoff);
                 __syncthreads();
                 buf ^= 1;
-                const int c2 = cc + 2;
+                const int c2 = cc + 1 + TL;
                 const int over = c2 >= nchunks;
                 int rsel[ACH];
 #pragma unroll
@@ -410,9 +422,10 @@ bool stream_ok(const ExpertArgs &a, bool gu)
     // as the routed experts
     if (a.I_shared != 0 && a.I_shared != a.I)
         return false;
+    // K in an even number of at least four 128-wide chunks
     if (gu)
-        return a.H % 256 == 0 && a.I % wrows_of(true) == 0;
-    return a.I % 256 == 0 && a.H % wrows_of(false) == 0;
+        return a.H % 256 == 0 && a.H >= 512 && a.I % wrows_of(true) == 0;
+    return a.I % 256 == 0 && a.I >= 512 && a.H % wrows_of(false) == 0;
 }
 
 int stream_wrows(bool gu) { return wrows_of(gu); }

@@ -111,4 +111,8 @@ struct CombineArgs {
 };
 void launch_combine(const CombineArgs &a, hipStream_t st);
 
+// Row-major bf16 [E, N, K] into the packed layout the bf16 GEMMs read
+// (packed_bf16_off in common.h).
+void launch_pack_bf16(int E, int N, int K, const uint16_t *w, uint16_t *out, hipStream_t st);
+
 }  // namespace moe

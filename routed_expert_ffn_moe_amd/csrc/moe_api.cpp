@@ -470,6 +470,22 @@ int moe_route(const moe_shape_t *s, const moe_weights_t *w, const void *x, int32
     return MOE_OK;
 }
 
+int moe_pack_bf16(int E, int N, int K, const void *w, void *w_out, void *stream)
+{
+    if (E < 1 || N < 32 || N % 32 || K < 32 || K % 32)
+        return fail(MOE_EINVAL, "moe_pack_bf16: E >= 1, N and K multiples of 32");
+    if (!w || !w_out)
+        return fail(MOE_EINVAL, "moe_pack_bf16: NULL pointer");
+    if (!aligned16(w) || !aligned16(w_out))
+        return fail(MOE_EINVAL, "moe_pack_bf16: pointer not 16-byte aligned");
+    const size_t nb = (size_t)E * N * K * 2;
+    const uintptr_t a = (uintptr_t)w, b = (uintptr_t)w_out;
+    if (a < b + nb && b < a + nb)
+        return fail(MOE_EINVAL, "moe_pack_bf16: output overlaps the input");
+    moe::launch_pack_bf16(E, N, K, (const uint16_t *)w, (uint16_t *)w_out, (hipStream_t)stream);
+    return launched("moe_pack_bf16");
+}
+
 int moe_pack_mxfp4(int E, int N, int K, const void *codes, const uint8_t *scales, void *codes_out,
                    uint8_t *scales_out, void *stream)
 {

@@ -68,13 +68,19 @@ class GpuLayer:
         self.router_bias = None if lay.router_bias is None else torch.from_numpy(lay.router_bias).to(dev)
         wg, wu, wd = lay.w_gate, lay.w_up, lay.w_down
         sg, su, sd = lay.s_gate, lay.s_up, lay.s_down
-        if c["w"] == "mxfp4":  # the layout the kernels read
+        shg, shu, shd = lay.sh_gate, lay.sh_up, lay.sh_down
+        # the layouts the kernels read
+        if c["w"] == "mxfp4":
             (wg, sg), (wu, su), (wd, sd) = (moe.pack_mxfp4(wg, sg), moe.pack_mxfp4(wu, su),
                                             moe.pack_mxfp4(wd, sd))
+        elif c["w"] == "bf16":
+            wg, wu, wd = moe.pack_bf16(wg), moe.pack_bf16(wu), moe.pack_bf16(wd)
+        if c["act"] == "bf16" and shg is not None:
+            shg, shu, shd = moe.pack_bf16(shg), moe.pack_bf16(shu), moe.pack_bf16(shd)
         self.weights = moe.make_weights(self.router_w, wg, wu, wd,
                                         router_bias=self.router_bias, s_gate=sg,
-                                        s_up=su, s_down=sd, sh_gate=lay.sh_gate,
-                                        sh_up=lay.sh_up, sh_down=lay.sh_down)
+                                        s_up=su, s_down=sd, sh_gate=shg,
+                                        sh_up=shu, sh_down=shd)
 
     def shape(self, T, chunk_T=0):
         c = self.c

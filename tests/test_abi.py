@@ -147,3 +147,18 @@ def test_pack_mxfp4_rejects_bad_arguments(E, N, K, ptrs):
     rc = lib.moe_pack_mxfp4(E, N, K, *[ctypes.c_void_p(p) for p in ptrs], None)
     assert rc == moe.MOE_EINVAL
     assert "moe_pack_mxfp4" in moe.moe_last_error()
+
+
+@pytest.mark.parametrize("E,N,K,ptrs", [
+    (0, 64, 64, (16, 1 << 20)),          # no experts
+    (2, 48, 64, (16, 1 << 20)),          # N not a multiple of 32
+    (2, 64, 80, (16, 1 << 20)),          # K not a multiple of 32
+    (2, 64, 64, (0, 1 << 20)),           # NULL input
+    (2, 64, 64, (16, (1 << 20) + 8)),    # misaligned output
+    (2, 64, 64, (1 << 20, (1 << 20) + 1024)),  # output overlaps the input
+])
+def test_pack_bf16_rejects_bad_arguments(E, N, K, ptrs):
+    lib = moe.load()
+    rc = lib.moe_pack_bf16(E, N, K, *[ctypes.c_void_p(p) for p in ptrs], None)
+    assert rc == moe.MOE_EINVAL
+    assert "moe_pack_bf16" in moe.moe_last_error()

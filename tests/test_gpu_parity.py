@@ -222,3 +222,26 @@ def test_pack_mxfp4_layout():
                     want_s[e, nb, lane, q] = s[e, n, k0 // 32]
     assert np.array_equal(pc.cpu().numpy().reshape(-1), want_c.reshape(-1))
     assert np.array_equal(ps.cpu().numpy().reshape(-1), want_s.reshape(-1))
+
+
+def test_pack_bf16_layout():
+    """The packed bf16 layout, element for element, against its definition in
+    the header: [E][N/32][K/32][2][64 lanes][8], lane r + 16*b of block c
+    holding row 32*g + 8*(r/4) + 4*c + r%4 at K = 32*s + 8*b .. +7."""
+    E, N, K = 2, 96, 160
+    g = torch.Generator().manual_seed(6)
+    w = torch.randint(-32768, 32767, (E, N, K), generator=g, dtype=torch.int16)
+    pw = moe.pack_bf16(w.view(torch.bfloat16).cuda())
+    torch.cuda.synchronize()
+    a = w.numpy()
+    want = np.empty((E, N // 32, K // 32, 2, 64, 8), np.int16)
+    for e in range(E):
+        for gg in range(N // 32):
+            for s in range(K // 32):
+                for c in range(2):
+                    for lane in range(64):
+                        r, b = lane % 16, lane // 16
+                        n = 32 * gg + 8 * (r // 4) + 4 * c + r % 4
+                        want[e, gg, s, c, lane] = a[e, n, 32 * s + 8 * b:32 * s + 8 * b + 8]
+    got = pw.view(torch.int16).cpu().numpy()
+    assert np.array_equal(got.reshape(-1), want.reshape(-1))
