@@ -109,11 +109,16 @@ __device__ __forceinline__ void rows_load(u32v<ACH> &r, const uint16_t *x, const
 // token row mb*16 + l16, K = 32*s4 + 8*lg .. +7.
 template <int NMB, int SLD>
 __device__ __forceinline__ void frag_load(bf16x8 (&tf)[NMB], const uint16_t *As, int s4, int l16,
-                                          int lg)
+                                          int lg, bool full)
 {
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+    for (int mb = 0; mb < NMB / 2; ++mb)
         tf[mb] = as_bf16x8(*(const uint4 *)(As + (mb * 16 + l16) * SLD + s4 * 32 + lg * 8));
+    if (full || NMB < 2) {
+#pragma unroll
+        for (int mb = NMB / 2; mb < NMB; ++mb)
+            tf[mb] = as_bf16x8(*(const uint4 *)(As + (mb * 16 + l16) * SLD + s4 * 32 + lg * 8));
+    }
 }
 
 // The SKC/32 K steps of a staged token chunk.  Step s consumes the weight
@@ -121,8 +126,10 @@ __device__ __forceinline__ void frag_load(bf16x8 (&tf)[NMB], const uint16_t *As,
 // ahead (chunk wl[(s + SD) / SPC], step (s + SD) % SPC); the token fragments
 // of step s + 1 are read from LDS before the MFMAs of step s run, so LDS
 // latency hides behind them.
+// With `full` false (uniform) only the first half of the MB token blocks is
+// read and multiplied: the rest of the item's row tile is empty.
 template <int MB, int NB, int CB, int SD, int SKC>
-__device__ __forceinline__ void kchunk(const uint16_t *As, int slot0, int l16, int lg,
+__device__ __forceinline__ void kchunk(bool full, const uint16_t *As, int slot0, int l16, int lg,
                                        uint4 (&bq)[SD][NB][CB],
                                        const uint16_t *const (&wl)[3][NB],
                                        const int (&woff)[CB], floatx4 (&acc)[NB][CB][MB])
@@ -130,7 +137,7 @@ __device__ __forceinline__ void kchunk(const uint16_t *As, int slot0, int l16, i
     constexpr int SPC = SKC / 32, SLD = sld_of(SKC);
     static_assert((SPC - 1 + SD) / SPC <= 2, "refills reach at most two chunks ahead");
     bf16x8 tf[2][MB];
-    frag_load<MB, SLD>(tf[0], As, 0, l16, lg);
+    frag_load<MB, SLD>(tf[0], As, 0, l16, lg, full);
 #pragma unroll
     for (int st = 0; st < SPC; ++st) {
         const int slot = (slot0 + st) % SD;
@@ -145,17 +152,26 @@ __device__ __forceinline__ void kchunk(const uint16_t *As, int slot0, int l16, i
                 bq[slot][m][cb] = *(const uint4 *)(w[m] + woff[cb] + wk * 32);
             }
         if (st + 1 < SPC)
-            frag_load<MB, SLD>(tf[(st + 1) & 1], As, st + 1, l16, lg);
+            frag_load<MB, SLD>(tf[(st + 1) & 1], As, st + 1, l16, lg, full);
         // issue the refills and the next fragments here, not later: the
         // waits for this step's operands must not have to wait for them
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB / 2; ++mb)
 #pragma unroll
             for (int m = 0; m < NB; ++m)
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb)
                     acc[m][cb][mb] = mfma16(wf[m][cb], tf[st & 1][mb], acc[m][cb][mb]);
+        if (full || MB < 2) {
+#pragma unroll
+            for (int mb = MB / 2; mb < MB; ++mb)
+#pragma unroll
+                for (int m = 0; m < NB; ++m)
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+                        acc[m][cb][mb] = mfma16(wf[m][cb], tf[st & 1][mb], acc[m][cb][mb]);
+        }
     }
 }
 
@@ -275,6 +291,7 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
                 for (int mb = 0; mb < MB; ++mb)
                     acc[m][cb][mb] = floatx4{0, 0, 0, 0};
 
+        const bool full = cur.nrows > BM / 2;  // uniform
         for (int c = 0; c < nchunks; c += 2) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -292,8 +309,10 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
                     for (int m = 0; m < NB; ++m)
                         wl[d][m] = (over ? wn[m] : wc[m]) + tk;
                 }
-                // Every row block is computed, also those past the item's rows.
-                kchunk<MB, NB, CB, SD, SKC>(As, h * SPC, l16, lg, bq, wl, woff, acc);
+                // Items whose rows fit the first half of the row tile skip
+                // the MFMAs of the second half (the tile's other empty row
+                // blocks are computed: finer splits cost more than they save).
+                kchunk<MB, NB, CB, SD, SKC>(full, As, h * SPC, l16, lg, bq, wl, woff, acc);
                 // Token chunk pipeline: rt[h % TL] holds the chunk after this
                 // one and is reloaded with the chunk TL + 1 ahead.
                 u32v<ACH> &ra = rt[h % TL];
