@@ -52,6 +52,42 @@ def stage_work(c, counts):
     }
 
 
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+
+
+def kernel_sources_sha1():
+    """Digest of the HIP sources: counter readings taken from other sources
+    no longer describe the kernels that run."""
+    import hashlib
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "routed_expert_ffn_moe_amd", "csrc")
+    h = hashlib.sha1()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of `stage` on `workload` from the committed
+    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, each scaled by its
+    reading for a plain copy), or None if there is none for the current
+    kernel sources."""
+    path = os.path.join(PROFILES, "hbm_traffic_counters.md")
+    if not os.path.exists(path):
+        return None
+    sha = kernel_sources_sha1()
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("<!-- traffic ") and line.endswith("-->"):
+            rec = json.loads(line[len("<!-- traffic "):-3])
+            if rec.get("workload") == workload and rec.get("stage") == stage \
+                    and rec.get("sources_sha1") == sha:
+                return int(rec["bytes"])
+    return None
+
+
 def roofline(work, stage, ms, dtype):
     byts, flops = work[stage]
     dur = ms / 1e3
@@ -270,7 +306,8 @@ def main():
                    "top_k": c["top_k"], "I": c["I"], "I_shared": c["I_shared"],
                    "bias": c["bias"], "experts_touched": work["_Es"],
                    "max_rows_per_expert": int(counts.max())},
-        "roofline": roofline(work, dom, stages[dom], c["w"]),
+        "roofline": dict(roofline(work, dom, stages[dom], c["w"]),
+                         traffic=measured_traffic(args.workload, dom)),
         "stages_us": {k: round(v * 1e3, 2) for k, v in stages.items()},
         "tuning": {k: v for k, v in os.environ.items() if k.startswith("MOE_")},
     }
@@ -298,7 +335,8 @@ def main():
                       "us_per_step": round(wall2 / steps * 1e6, 2), **entry, "weight_sets": wsets,
                       "experts_touched": wk["_Es"],
                       "stages_us": {k: round(v * 1e3, 2) for k, v in st2.items()},
-                      "roofline": roofline(wk, d2, st2[d2], cc["w"])}
+                      "roofline": dict(roofline(wk, d2, st2[d2], cc["w"]),
+                                       traffic=measured_traffic(name, d2))}
         del w2
         torch.cuda.empty_cache()
     out["also"] = also
