@@ -264,31 +264,7 @@ __global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__
     if (i >= (int64_t)T * per_row)
         return;
     const int t = (int)(i / per_row), c8 = (int)(i % per_row) * 8;
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    const int n_rows = k + (shared ? 1 : 0);
-    for (int j = 0; j < n_rows; ++j) {
-        int64_t row;
-        float w;
-        if (j < k) {
-            row = row_of[(int64_t)t * k + j];
-            w = topk_w[(int64_t)t * k + j];
-        } else {
-            row = (int64_t)T * k + t;
-            w = 1.0f;
-        }
-        const uint4 v = *(const uint4 *)(stage + row * H + c8);
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            acc[2 * q] = fmaf(w, bf2f((uint16_t)(w4[q] & 0xFFFF)), acc[2 * q]);
-            acc[2 * q + 1] = fmaf(w, bf2f((uint16_t)(w4[q] >> 16)), acc[2 * q + 1]);
-        }
-    }
-    uint4 o;
-    o.x = pack_bf2(acc[0], acc[1]);
-    o.y = pack_bf2(acc[2], acc[3]);
-    o.z = pack_bf2(acc[4], acc[5]);
-    o.w = pack_bf2(acc[6], acc[7]);
+    const uint4 o = combine_row8(stage, row_of, topk_w, t, T, H, k, shared, c8);
     *(uint4 *)(y + (int64_t)t * H + c8) = o;
 }
 

@@ -55,6 +55,21 @@ struct StreamP {
     int T, H, E, k, I, Is, ldh, ntn;
 };
 
+// A weight fragment.  With NT the load is non-temporal: small row tiles
+// read each weight once, and keeping those lines out of the caches leaves
+// room for the token rows (measured faster there, slower for large tiles
+// whose weights are re-read by several row tiles).
+template <bool NT>
+__device__ __forceinline__ uint4 wload(const uint16_t *p)
+{
+    if (NT) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 v = __builtin_nontemporal_load((const u32x4 *)p);
+        return uint4{v[0], v[1], v[2], v[3]};
+    }
+    return *(const uint4 *)p;
+}
+
 template <int N>
 __device__ __forceinline__ void chunk_store(const u32v<N> &r, uint16_t *dst, const int (&off)[N])
 {
@@ -149,7 +164,7 @@ __device__ __forceinline__ void kchunk(bool full, const uint16_t *As, int slot0,
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
                 wf[m][cb] = as_bf16x8(bq[slot][m][cb]);
-                bq[slot][m][cb] = *(const uint4 *)(w[m] + woff[cb] + wk * 32);
+                bq[slot][m][cb] = wload<(MB <= 2)>(w[m] + woff[cb] + wk * 32);
             }
         if (st + 1 < SPC)
             frag_load<MB, SLD>(tf[(st + 1) & 1], As, st + 1, l16, lg, full);
@@ -256,7 +271,7 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
         for (int m = 0; m < NB; ++m)
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb)
-                bq[d][m][cb] = *(const uint4 *)(wc[m] + woff[cb] + d * 1024);  // SD <= 8 <= K/32
+                bq[d][m][cb] = wload<(MB <= 2)>(wc[m] + woff[cb] + d * 1024);  // SD <= 8 <= K/32
     int aro[ACH], aro_n[ACH];
     item_rows<ACH, GU, SKC>(p, cur, tid, aro);
     item_rows<ACH, GU, SKC>(p, nxt, tid, aro_n);

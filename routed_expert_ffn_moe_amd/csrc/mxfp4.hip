@@ -391,12 +391,13 @@ template <bool GU, int CPW, int NW, int NQ>
 void launch(const MxP &p, int N, int K, int tiles, hipStream_t st)
 {
     const size_t lds = (size_t)p.cap * (2 * (K + MX_PAD) + 2 * (K / 32));
-    static bool attr = false;
-    if (!attr) {
-        (void)hipFuncSetAttribute((const void *)expert_mxfp4<GU, CPW, NW, NQ>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        attr = true;
-    }
+    // Dynamic LDS above the default limit is granted per size; a failure
+    // here is left to the launch below to report.
+    static size_t granted = 48 * 1024;
+    if (lds > granted &&
+        hipFuncSetAttribute((const void *)expert_mxfp4<GU, CPW, NW, NQ>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess)
+        granted = lds;
     expert_mxfp4<GU, CPW, NW, NQ>
         <<<dim3(N / (16 * CPW * NW), tiles), 64 * NW, lds, st>>>(p, p.ntiles, p.tiles, p.offsets,
                                                                    p.row_tok);
