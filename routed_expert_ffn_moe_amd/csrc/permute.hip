@@ -10,15 +10,27 @@
 // "MoE prefill quantum" (cause section: tokens per expert set the cost).
 //
 // Determinism: counts use LDS atomics (order-free); positions come from
-// ballot-based ranks inside one wave that walks its block's pairs in order,
-// so the grouped order is t ascending, then j, within every expert, the same
-// as a stable counting sort.
+// ballot-based ranks inside waves that walk their pairs in order, so the
+// grouped order is t ascending, then j, within every expert, the same as a
+// stable counting sort.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
 constexpr int PAIRS_PER_BLOCK = 1024;
+// Passes whose per-block histograms fit in this many LDS counters build them
+// inside the scan kernel (one launch less).
+constexpr int FUSED_HIST = 8192;
+
+// Orders one wave's LDS accesses across its lanes (no other wave shares
+// the data).
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
 
 int permute_blocks(int n_pairs)
 {
@@ -48,26 +60,57 @@ __global__ __launch_bounds__(256) void permute_hist(const int32_t *__restrict__ 
 
 // One workgroup: counts, offsets (exclusive prefix in LDS), per-block start
 // positions (written over blk), the shared-expert group and both tile lists.
+// With idx given (nblk * E <= FUSED_HIST) it counts the blocks' pairs itself.
 __global__ __launch_bounds__(1024) void permute_scan(
+    const int32_t *__restrict__ idx,
     int32_t *__restrict__ blk, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     Tile *__restrict__ tiles_a, int32_t *__restrict__ ntiles_a, Tile *__restrict__ tiles_b,
     int32_t *__restrict__ ntiles_b, int bm_a, int bm_b, int nblk, int E, int n_pairs, int T,
-    int shared)
+    int shared, int4 *__restrict__ items_a, int ntn_a, int wrows_a, int4 *__restrict__ items_b,
+    int ntn_b, int wrows_b)
 {
     __shared__ int32_t s_cnt[1025];
     __shared__ int32_t s_ta[1025];
     __shared__ int32_t s_tb[1025];
     __shared__ int32_t s_off[1025];
     __shared__ int32_t s_warp[3][16];
+    __shared__ int32_t s_blk[FUSED_HIST];
     const int tid = threadIdx.x;
     const int G = E + (shared ? 1 : 0);  // groups
-    // Column sums over blocks; blk[b][e] becomes the running prefix.
+    constexpr int SCH = 16;
+    if (idx) {
+        // Per-block histograms in LDS, then their running prefixes in place.
+        for (int i = tid; i < nblk * E; i += 1024)
+            s_blk[i] = 0;
+        __syncthreads();
+        for (int p = tid; p < n_pairs; p += 1024)
+            atomicAdd(&s_blk[(p / PAIRS_PER_BLOCK) * E + idx[p]], 1);
+        __syncthreads();
+        for (int e = tid; e < E; e += 1024) {
+            int run = 0;
+            for (int b = 0; b < nblk; ++b) {
+                const int c = s_blk[b * E + e];
+                s_blk[b * E + e] = run;
+                run += c;
+            }
+            s_cnt[e] = run;
+        }
+    } else
+    // Column sums over blocks (the block counts are read SCH at a time, all
+    // in flight together); blk[b][e] becomes the running prefix.
     for (int e = tid; e < E; e += 1024) {
         int run = 0;
-        for (int b = 0; b < nblk; ++b) {
-            int c = blk[(int64_t)b * E + e];
-            blk[(int64_t)b * E + e] = run;
-            run += c;
+        for (int b0 = 0; b0 < nblk; b0 += SCH) {
+            int c[SCH];
+#pragma unroll
+            for (int i = 0; i < SCH; ++i)
+                c[i] = b0 + i < nblk ? blk[(int64_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < SCH; ++i)
+                if (b0 + i < nblk) {
+                    blk[(int64_t)(b0 + i) * E + e] = run;
+                    run += c[i];
+                }
         }
         s_cnt[e] = run;
     }
@@ -119,110 +162,146 @@ __global__ __launch_bounds__(1024) void permute_scan(
     __syncthreads();
     // Per-block start positions inside each expert's range.
     for (int e = tid; e < E; e += 1024) {
-        int o = s_off[e];
-        for (int b = 0; b < nblk; ++b)
-            blk[(int64_t)b * E + e] += o;
+        const int o = s_off[e];
+        if (idx) {
+            for (int b = 0; b < nblk; ++b)
+                blk[(int64_t)b * E + e] = s_blk[b * E + e] + o;
+            continue;
+        }
+        for (int b0 = 0; b0 < nblk; b0 += SCH) {
+            int c[SCH];
+#pragma unroll
+            for (int i = 0; i < SCH; ++i)
+                c[i] = b0 + i < nblk ? blk[(int64_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < SCH; ++i)
+                if (b0 + i < nblk)
+                    blk[(int64_t)(b0 + i) * E + e] = c[i] + o;
+        }
     }
-    // Tile lists.
+    // Tile lists, and the work items of the streaming GEMMs: expert-major,
+    // then column tile, then row tile, so that item lists dealt out in
+    // contiguous runs keep an expert on one XCD.
     for (int g = tid; g < G; g += 1024) {
-        int cg = g < E ? s_cnt[g] : T;
-        int og = s_off[g];
-        for (int r = 0, t = s_ta[g]; r < cg; r += bm_a, ++t)
-            tiles_a[t] = Tile{g, og + r};
-        for (int r = 0, t = s_tb[g]; r < cg; r += bm_b, ++t)
-            tiles_b[t] = Tile{g, og + r};
+        const int cg = g < E ? s_cnt[g] : T;
+        const int og = s_off[g];
+        const int na = (cg + bm_a - 1) / bm_a, nb = (cg + bm_b - 1) / bm_b;
+        for (int m = 0; m < na; ++m)
+            tiles_a[s_ta[g] + m] = Tile{g, og + m * bm_a};
+        for (int m = 0; m < nb; ++m)
+            tiles_b[s_tb[g] + m] = Tile{g, og + m * bm_b};
     }
+    if (items_a)
+        for (int q = tid; q < G * ntn_a; q += 1024) {
+            const int g = q / ntn_a, nt = q - g * ntn_a;
+            const int cg = g < E ? s_cnt[g] : T, og = s_off[g];
+            const int na = (cg + bm_a - 1) / bm_a;
+            for (int m = 0; m < na; ++m)
+                items_a[ntn_a * s_ta[g] + nt * na + m] =
+                    int4{g, og + m * bm_a, min(bm_a, cg - m * bm_a), nt * wrows_a};
+        }
+    if (items_b)
+        for (int q = tid; q < G * ntn_b; q += 1024) {
+            const int g = q / ntn_b, nt = q - g * ntn_b;
+            const int cg = g < E ? s_cnt[g] : T, og = s_off[g];
+            const int nb = (cg + bm_b - 1) / bm_b;
+            for (int m = 0; m < nb; ++m)
+                items_b[ntn_b * s_tb[g] + nt * nb + m] =
+                    int4{g, og + m * bm_b, min(bm_b, cg - m * bm_b), nt * wrows_b};
+        }
 }
 
-// Stable scatter.  One wave per block walks the block's pairs 64 at a time in
-// pair order; lanes with equal experts are ranked by lane index from a
-// ballot-built match mask, and the lowest such lane advances the expert's
-// running position in LDS.
-__global__ __launch_bounds__(64) void permute_scatter(const int32_t *__restrict__ idx,
-                                                     const int32_t *__restrict__ blk,
-                                                     int32_t *__restrict__ row_src,
-                                                     int32_t *__restrict__ row_tok,
-                                                     int32_t *__restrict__ row_of, int n_pairs,
-                                                     int E, int T, int k, int shared)
+// Stable scatter.  Each of a block's 4 waves walks a quarter of its pairs 64
+// at a time in pair order, starting every expert after the earlier quarters'
+// pairs of that expert (integer LDS counts); lanes with equal experts are
+// ranked by lane index from a ballot-built match mask, and the lowest such
+// lane advances the expert's running position.
+__global__ __launch_bounds__(256) void permute_scatter(const int32_t *__restrict__ idx,
+                                                      const int32_t *__restrict__ blk,
+                                                      int32_t *__restrict__ row_src,
+                                                      int32_t *__restrict__ row_tok,
+                                                      int32_t *__restrict__ row_of, int n_pairs,
+                                                      int E, int T, int k, int shared)
 {
+    // run[w * E + e]: next position of expert e for wave w, which owns the
+    // block's pairs w*256 .. +255 (a quarter, in pair order).
     extern __shared__ int32_t run[];
-    const int lane = threadIdx.x;
-    for (int e = lane; e < E; e += 64)
-        run[e] = blk[(int64_t)blockIdx.x * E + e];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int base = blockIdx.x * PAIRS_PER_BLOCK + wave * (PAIRS_PER_BLOCK / 4);
+    constexpr int NS = PAIRS_PER_BLOCK / 4 / 64;
+    int ev[NS];  // this wave's experts, all loads in flight at once
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const int p = base + 64 * i + lane;
+        ev[i] = p < n_pairs ? idx[p] : -1;
+    }
+    for (int i = threadIdx.x; i < 4 * E; i += 256)
+        run[i] = 0;
     __syncthreads();
-    const int base = blockIdx.x * PAIRS_PER_BLOCK;
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+        if (ev[i] >= 0)
+            atomicAdd(&run[wave * E + ev[i]], 1);  // integer counts: order-free
+    __syncthreads();
+    // Each wave starts after the earlier quarters' pairs of the same expert.
+    for (int e = threadIdx.x; e < E; e += 256) {
+        int pos = blk[(int64_t)blockIdx.x * E + e];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int c = run[w * E + e];
+            run[w * E + e] = pos;
+            pos += c;
+        }
+    }
+    __syncthreads();
+    int32_t *wrun = run + wave * E;
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int s = 0; s < PAIRS_PER_BLOCK; s += 64) {
-        const int p = base + s + lane;
-        const bool valid = p < n_pairs;
-        const int e = valid ? idx[p] : 0;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const int p = base + 64 * i + lane;
+        const int e = ev[i];
+        const bool valid = e >= 0;
         uint64_t match = __ballot(valid);
         for (int bit = 0; bit < 10; ++bit) {
-            uint64_t ones = __ballot(valid && ((e >> bit) & 1));
+            const uint64_t ones = __ballot(valid && ((e >> bit) & 1));
             match &= ((e >> bit) & 1) ? ones : ~ones;
         }
         const int rank = __popcll(match & lt);
         int pos = 0;
         if (valid)
-            pos = run[e] + rank;
-        __syncthreads();
+            pos = wrun[e] + rank;
+        wave_lds_sync();
         if (valid) {
             row_src[pos] = p;
             row_tok[pos] = p / k;
             row_of[p] = pos;
             if (rank == 0)
-                run[e] += __popcll(match);
+                wrun[e] += __popcll(match);
         }
-        __syncthreads();
+        wave_lds_sync();
     }
     // Shared-expert rows follow the routed ones, in token order.
     if (shared && blockIdx.x == 0) {
-        for (int t = lane; t < T; t += 64) {
+        for (int t = threadIdx.x; t < T; t += 256) {
             row_src[n_pairs + t] = n_pairs + t;
             row_tok[n_pairs + t] = t;
         }
     }
 }
 
-// Work items of the streaming GEMMs, one thread per (tile, column tile):
-// expert-major, then column tile, then row tile, so that item lists dealt out
-// in contiguous runs keep an expert on one XCD.  The tiles of expert g start
-// at s_g = tile index - its rank inside the expert; its items at ntn * s_g.
-__global__ __launch_bounds__(256) void permute_items(const Tile *__restrict__ tiles,
-                                                     const int32_t *__restrict__ ntiles,
-                                                     const int32_t *__restrict__ offsets, int bm,
-                                                     int ntn, int wrows, int4 *__restrict__ items)
-{
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    const int n_t = *ntiles;
-    const int tau = i / ntn, nt = i - tau * ntn;
-    if (tau >= n_t)
-        return;
-    const Tile tl = tiles[tau];
-    const int og = offsets[tl.g], cg = offsets[tl.g + 1] - og;
-    const int rank = (tl.row0 - og) / bm;
-    const int sg = tau - rank;
-    const int na = (cg + bm - 1) / bm;
-    items[ntn * sg + nt * na + rank] = int4{tl.g, tl.row0, min(bm, cg - (tl.row0 - og)), nt * wrows};
-}
-
 void launch_permute(const PermuteArgs &a, hipStream_t st)
 {
     const int n_pairs = a.T * a.k;
     const int nblk = permute_blocks(n_pairs);
-    if (nblk > 0)
+    const bool fused = nblk * a.E <= FUSED_HIST;
+    if (nblk > 0 && !fused)
         permute_hist<<<nblk, 256, a.E * sizeof(int32_t), st>>>(a.idx, a.blk, n_pairs, a.E);
-    permute_scan<<<1, 1024, 0, st>>>(a.blk, a.counts, a.offsets, a.tiles_a, a.ntiles_a, a.tiles_b,
-                                     a.ntiles_b, a.bm_a, a.bm_b, nblk, a.E, n_pairs, a.T, a.shared);
+    permute_scan<<<1, 1024, 0, st>>>(fused ? a.idx : nullptr, a.blk, a.counts, a.offsets, a.tiles_a, a.ntiles_a, a.tiles_b,
+                                     a.ntiles_b, a.bm_a, a.bm_b, nblk, a.E, n_pairs, a.T, a.shared,
+                                     a.items_a, a.ntn_a, a.wrows_a, a.items_b, a.ntn_b, a.wrows_b);
     if (nblk > 0)
-        permute_scatter<<<nblk, 64, a.E * sizeof(int32_t), st>>>(
+        permute_scatter<<<nblk, 256, 4 * a.E * sizeof(int32_t), st>>>(
             a.idx, a.blk, a.row_src, a.row_tok, a.row_of, n_pairs, a.E, a.T, a.k, a.shared);
-    if (a.items_a && a.max_tiles_a > 0)
-        permute_items<<<(a.max_tiles_a * a.ntn_a + 255) / 256, 256, 0, st>>>(
-            a.tiles_a, a.ntiles_a, a.offsets, a.bm_a, a.ntn_a, a.wrows_a, a.items_a);
-    if (a.items_b && a.max_tiles_b > 0)
-        permute_items<<<(a.max_tiles_b * a.ntn_b + 255) / 256, 256, 0, st>>>(
-            a.tiles_b, a.ntiles_b, a.offsets, a.bm_b, a.ntn_b, a.wrows_b, a.items_b);
 }
 
 }  // namespace moe
