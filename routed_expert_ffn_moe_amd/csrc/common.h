@@ -49,6 +49,24 @@ __device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// The same MFMA with the accumulator held in the accumulation registers and
+// updated in place.  For kernels whose accumulators fill those registers:
+// there the compiler's own allocation rotates them through copies between
+// MFMAs, which cost more issue slots than the MFMAs themselves.  The
+// instruction is opaque to the compiler's hazard tracking, so ordinary
+// instructions may read these accumulators only after mfma_acc_drain().
+__device__ __forceinline__ void mfma16_acc(floatx4 &c, bf16x8 a, bf16x8 b)
+{
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// Wait states covering the longest MFMA result latency before other
+// instructions read mfma16_acc results.
+__device__ __forceinline__ void mfma_acc_drain()
+{
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v)
 {
     return __builtin_bit_cast(bf16x8, v);

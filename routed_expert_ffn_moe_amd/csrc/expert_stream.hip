@@ -143,7 +143,19 @@ __device__ __forceinline__ void frag_load(bf16x8 (&tf)[NMB], const uint16_t *As,
 // latency hides behind them.
 // With `full` false (uniform) only the first half of the MB token blocks is
 // read and multiplied: the rest of the item's row tile is empty.
-template <int MB, int NB, int CB, int SD, int SKC>
+// One MFMA step into an accumulator: in place in the accumulation
+// registers (AGPR) for the large row tiles, whose accumulators live there,
+// else the compiler's own form.
+template <bool AGPR>
+__device__ __forceinline__ void mac(floatx4 &c, bf16x8 a, bf16x8 b)
+{
+    if (AGPR)
+        mfma16_acc(c, a, b);
+    else
+        c = mfma16(a, b, c);
+}
+
+template <int MB, int NB, int CB, int SD, int SKC, bool AGPR>
 __device__ __forceinline__ void kchunk(bool full, const uint16_t *As, int slot0, int l16, int lg,
                                        uint4 (&bq)[SD][NB][CB],
                                        const uint16_t *const (&wl)[3][NB],
@@ -177,7 +189,7 @@ __device__ __forceinline__ void kchunk(bool full, const uint16_t *As, int slot0,
             for (int m = 0; m < NB; ++m)
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb)
-                    acc[m][cb][mb] = mfma16(wf[m][cb], tf[st & 1][mb], acc[m][cb][mb]);
+                    mac<AGPR>(acc[m][cb][mb], wf[m][cb], tf[st & 1][mb]);
         if (full || MB < 2) {
 #pragma unroll
             for (int mb = MB / 2; mb < MB; ++mb)
@@ -185,7 +197,7 @@ __device__ __forceinline__ void kchunk(bool full, const uint16_t *As, int slot0,
                 for (int m = 0; m < NB; ++m)
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb)
-                        acc[m][cb][mb] = mfma16(wf[m][cb], tf[st & 1][mb], acc[m][cb][mb]);
+                        mac<AGPR>(acc[m][cb][mb], wf[m][cb], tf[st & 1][mb]);
         }
     }
 }
@@ -213,6 +225,8 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
     static_assert((2 * SPC) % SD == 0, "ring slots line up with chunk pairs");
     static_assert(ACH >= 1 && ACH * 256 == BM * SKC / 8, "token staging");
     static_assert(CB % 2 == 0 && 4 * CB * 16 == wrows_of(GU), "column blocks go in pairs");
+    // the 128-row tiles' accumulators fill the accumulation registers
+    constexpr bool AGPR = BM >= 128;
 
     __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * SLD];
 
@@ -327,7 +341,7 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
                 // Items whose rows fit the first half of the row tile skip
                 // the MFMAs of the second half (the tile's other empty row
                 // blocks are computed: finer splits cost more than they save).
-                kchunk<MB, NB, CB, SD, SKC>(full, As, h * SPC, l16, lg, bq, wl, woff, acc);
+                kchunk<MB, NB, CB, SD, SKC, AGPR>(full, As, h * SPC, l16, lg, bq, wl, woff, acc);
                 // Token chunk pipeline: rt[h % TL] holds the chunk after this
                 // one and is reloaded with the chunk TL + 1 ahead.
                 u32v<ACH> &ra = rt[h % TL];
@@ -347,6 +361,8 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
             }
         }
 
+        if (AGPR)
+            mfma_acc_drain();
         // Epilogue: for block pair q the lane holds columns n + 32q .. +7 of
         // token row mb*16 + l16 (block 2q covers the first four).
         const int n = cur.n0 + wave * 16 * CB + lg * 8;

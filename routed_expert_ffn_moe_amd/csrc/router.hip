@@ -60,21 +60,25 @@ __global__ __launch_bounds__(64 * WN) void router_logits_bf16(
 }
 
 // bf16 logits for T > 16: a workgroup owns RT tokens x 64 experts.  The
-// token rows are staged in LDS in double-buffered 128-wide K chunks; each wave
-// streams its 16 expert rows from global memory through an 8-step register
-// ring (no barrier on that path).  The MFMA takes the expert rows as its A
-// operand, so a lane ends up with 4 consecutive experts of one token and
-// stores them as one 16-byte word.  Every logit is the sequential sum over K
-// in 32-wide MFMA steps, whatever RT and the grid are.
+// token rows are staged in LDS in double-buffered 128-wide K chunks, with
+// RTL more chunks in flight in registers; each wave streams its 16 expert
+// rows from global memory through a 16-step register ring (no barrier on
+// that path).  The GEMM does two MFMAs per 1 KB of weights a wave loads, so
+// it runs at the pace its loads arrive: the chunk queue and the ring keep
+// about 100 KB per workgroup in flight.  The MFMA takes the expert rows as
+// its A operand, so a lane ends up with 4 consecutive experts of one token
+// and stores them as one 16-byte word.  Every logit is the sequential sum
+// over K in 32-wide MFMA steps, whatever RT and the grid are.
 constexpr int RKC = 128;        // K chunk staged in LDS
 constexpr int RLD = RKC + 8;    // padded LDS row (bf16)
-constexpr int RSD = 8;          // weight prefetch ring (K steps)
+constexpr int RTL = 4;          // token chunks in flight in registers
+constexpr int RSD = 4 * RTL;    // weight prefetch ring (K steps): RTL chunks
 
 template <int RT>
-__global__ __launch_bounds__(256) void router_gemm(const uint16_t *__restrict__ x,
-                                                   const uint16_t *__restrict__ wr,
-                                                   const float *__restrict__ bias,
-                                                   float *__restrict__ logits, int T, int H, int E)
+__global__ __launch_bounds__(256, 1) void router_gemm(const uint16_t *__restrict__ x,
+                                                      const uint16_t *__restrict__ wr,
+                                                      const float *__restrict__ bias,
+                                                      float *__restrict__ logits, int T, int H, int E)
 {
     constexpr int MB = RT / 16;              // token blocks
     constexpr int XCH = RT * (RKC / 8) / 256; // 16-byte token chunks per thread
@@ -92,31 +96,32 @@ __global__ __launch_bounds__(256) void router_gemm(const uint16_t *__restrict__ 
         xo[i] = min(t0 + r, T - 1) * H + c8 * 8;
         so[i] = r * RLD + c8 * 8;
     }
-    const int nsteps = H / 32, nchunks = H / RKC;  // nchunks even
+    const int nsteps = H / 32, nchunks = H / RKC;  // nchunks a multiple of RTL
     uint4 bq[RSD];
 #pragma unroll
     for (int d = 0; d < RSD; ++d)
         bq[d] = *(const uint4 *)(wp + min(d, nsteps - 1) * 32);
-    u32v<XCH> ra;
+    // chunk q waits in slot q % RTL (one vector value: no scratch)
+    u32v<RTL * XCH> ra;
 #pragma unroll
     for (int i = 0; i < XCH; ++i)
-        vset<XCH>(ra, i, *(const uint4 *)(x + xo[i]));
+        *(uint4 *)(&sX[0][so[i]]) = *(const uint4 *)(x + xo[i]);
 #pragma unroll
-    for (int i = 0; i < XCH; ++i)
-        *(uint4 *)(&sX[0][so[i]]) = vget<XCH>(ra, i);
+    for (int q = 1; q <= RTL; ++q)
+#pragma unroll
+        for (int i = 0; i < XCH; ++i)
+            vset<RTL * XCH>(ra, (q % RTL) * XCH + i,
+                            *(const uint4 *)(x + xo[i] + min(q, nchunks - 1) * RKC));
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < XCH; ++i)
-        vset<XCH>(ra, i, *(const uint4 *)(x + xo[i] + min(1, nchunks - 1) * RKC));
     __builtin_amdgcn_sched_barrier(0);
     floatx4 acc[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
         acc[mb] = floatx4{0, 0, 0, 0};
     int buf = 0;
-    for (int c = 0; c < nchunks; c += 2) {
+    for (int c = 0; c < nchunks; c += RTL) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < RTL; ++h) {
             const int cc = c + h;
             const uint16_t *Xs = sX[buf];
 #pragma unroll
@@ -132,14 +137,18 @@ __global__ __launch_bounds__(256) void router_gemm(const uint16_t *__restrict__ 
                     acc[mb] = mfma16(wf, tf, acc[mb]);
                 }
             }
+            // chunk cc + 1 into the other buffer, then its slot takes chunk
+            // cc + 1 + RTL
+            const int sl = (h + 1) % RTL;  // a constant once h is unrolled
 #pragma unroll
             for (int i = 0; i < XCH; ++i)
-                *(uint4 *)(&sX[buf ^ 1][so[i]]) = vget<XCH>(ra, i);
+                *(uint4 *)(&sX[buf ^ 1][so[i]]) = vget<RTL * XCH>(ra, sl * XCH + i);
             __syncthreads();
             buf ^= 1;
 #pragma unroll
             for (int i = 0; i < XCH; ++i)
-                vset<XCH>(ra, i, *(const uint4 *)(x + xo[i] + min(cc + 2, nchunks - 1) * RKC));
+                vset<RTL * XCH>(ra, sl * XCH + i,
+                                *(const uint4 *)(x + xo[i] + min(cc + 1 + RTL, nchunks - 1) * RKC));
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -194,7 +203,7 @@ void launch_router_logits(const RouterArgs &a, hipStream_t st)
 {
     if (a.T == 0)
         return;
-    if (a.act == ACT_BF16 && a.T > 16 && a.E % 64 == 0 && a.H % 256 == 0) {
+    if (a.act == ACT_BF16 && a.T > 16 && a.E % 64 == 0 && a.H % (RKC * RTL) == 0) {
         // 64 tokens per workgroup for long chunks, 32 otherwise (more workgroups)
         if (a.T >= 4096) {
             dim3 grid(a.E / 64, (a.T + 63) / 64);

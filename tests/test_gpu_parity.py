@@ -80,10 +80,14 @@ def test_forward_parity(name):
     assert err <= hx.TOL[c["w"]], err
 
 
-@pytest.mark.parametrize("name", ["c1", "c2"])
-def test_route_and_permutation_bit_exact(name):
-    say("[route]", name)
+@pytest.mark.parametrize("name,T", [("c1", None), ("c2", None), ("c1", 9000)])
+def test_route_and_permutation_bit_exact(name, T):
+    """T=9000 at top-8 is 72,000 pairs: past the one-workgroup permutation,
+    so the multi-block histogram / scan / scatter path runs."""
+    say("[route]", name, T)
     c, g = layer(name)
+    if T is not None:
+        c = dict(c, T=T, seed=2000 + T)
     x = hx.margin_x(c, g.lay)
     idx, w, counts, offsets, row_src = g.route(hx.act_torch(x, c["act"], "cuda"))
     idx_h = idx.cpu().numpy()
