@@ -223,12 +223,8 @@ __device__ __forceinline__ void mx_step(const uint4 (&b)[NB][CPW], const int (&s
 // The tile list, its length and the group offsets come in as read-only
 // kernel arguments: uniform scalar loads, the first two issued together, so
 // a workgroup starts its weight stream one memory latency after it starts.
-// Workgroups per CU the register budget is held to: slabs of at most 16
-// 16-byte fragments per lane leave room for three.
-constexpr int mx_wg_per_cu(int nb, int cpw, int nq) { return nb * cpw * nq <= 16 ? 3 : 2; }
-
 template <bool GU, int CPW, int NW, int NQ>
-__global__ __launch_bounds__(64 * NW, mx_wg_per_cu(GU ? 2 : 1, CPW, NQ)) void expert_mxfp4(MxP p, const int32_t *__restrict__ ntiles,
+__global__ __launch_bounds__(64 * NW, 2) void expert_mxfp4(MxP p, const int32_t *__restrict__ ntiles,
                                                            const Tile *__restrict__ tiles,
                                                            const int32_t *__restrict__ offsets,
                                                            const int32_t *__restrict__ row_tok)
@@ -407,14 +403,15 @@ void launch(const MxP &p, int N, int K, int tiles, hipStream_t st)
                                                                    p.row_tok);
 }
 
-// Slab width (in 128-wide K steps): 8 where it divides K / 128 (slabs of
-// 8 leave room for three workgroups per CU, so a decode-sized grid fits the
-// chip in one round), else the largest of 6, 4, 2, 1 that does.
+// Slab width (in 128-wide K steps): the largest of 16, 8, 6, 4, 2, 1 that
+// divides K / 128.
 template <bool GU, int CPW, int NW>
 void launch_k(const MxP &p, int N, int K, int tiles, hipStream_t st)
 {
     const int q = K / 128;
-    if (q % 8 == 0)
+    if (q % 16 == 0)
+        launch<GU, CPW, NW, 16>(p, N, K, tiles, st);
+    else if (q % 8 == 0)
         launch<GU, CPW, NW, 8>(p, N, K, tiles, st);
     else if (q % 6 == 0)
         launch<GU, CPW, NW, 6>(p, N, K, tiles, st);
