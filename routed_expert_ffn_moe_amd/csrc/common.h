@@ -53,11 +53,13 @@ __device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c)
 // updated in place.  For kernels whose accumulators fill those registers:
 // there the compiler's own allocation rotates them through copies between
 // MFMAs, which cost more issue slots than the MFMAs themselves.  The
-// instruction is opaque to the compiler's hazard tracking, so ordinary
-// instructions may read these accumulators only after mfma_acc_drain().
+// instruction is opaque to the compiler's hazard tracking, so it carries its
+// own wait states for A/B operands written by a vector ALU instruction just
+// before it (two are required), and ordinary instructions may read these
+// accumulators only after mfma_acc_drain().
 __device__ __forceinline__ void mfma16_acc(floatx4 &c, bf16x8 a, bf16x8 b)
 {
-    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
 // Wait states covering the longest MFMA result latency before other
