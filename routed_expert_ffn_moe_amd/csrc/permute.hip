@@ -83,8 +83,20 @@ __global__ __launch_bounds__(1024) void permute_scan(
         for (int i = tid; i < nblk * E; i += 1024)
             s_blk[i] = 0;
         __syncthreads();
-        for (int p = tid; p < n_pairs; p += 1024)
-            atomicAdd(&s_blk[(p / PAIRS_PER_BLOCK) * E + idx[p]], 1);
+        // the pairs' experts are loaded PB at a time, all in flight together
+        constexpr int PB = 16;
+        for (int p0 = tid; p0 < n_pairs; p0 += 1024 * PB) {
+            int ev[PB];
+#pragma unroll
+            for (int i = 0; i < PB; ++i) {
+                const int p = p0 + 1024 * i;
+                ev[i] = p < n_pairs ? idx[p] : -1;
+            }
+#pragma unroll
+            for (int i = 0; i < PB; ++i)
+                if (ev[i] >= 0)
+                    atomicAdd(&s_blk[((p0 + 1024 * i) / PAIRS_PER_BLOCK) * E + ev[i]], 1);
+        }
         __syncthreads();
         for (int e = tid; e < E; e += 1024) {
             int run = 0;
