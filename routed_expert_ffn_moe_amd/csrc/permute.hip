@@ -151,10 +151,12 @@ __global__ __launch_bounds__(1024) void permute_scan(
     }
     __syncthreads();
     int pc = 0, pa = 0, pb = 0;
-    for (int w = 0; w < wv; ++w) {
-        pc += s_warp[0][w];
-        pa += s_warp[1][w];
-        pb += s_warp[2][w];
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {  // all reads in flight together
+        const bool in = w < wv;
+        pc += in ? s_warp[0][w] : 0;
+        pa += in ? s_warp[1][w] : 0;
+        pb += in ? s_warp[2][w] : 0;
     }
     const int exc = pc + ic - c, exa = pa + ia - va, exb = pb + ib - vb;
     if (tid < G) {

@@ -2,8 +2,8 @@
 // 16 tokens and 256 (token, slot) pairs): two launches instead of seven.
 //
 //  router_small: logits of <= 16 tokens; each workgroup owns 16 experts and
-//                its 4 waves split K in quarters, then add their partial sums
-//                in a fixed order (deterministic).
+//                its 8 (or 4) waves split K, then add their partial sums in
+//                a fixed order (deterministic).
 //  route_small:  one workgroup: top-k and weights of every token, then the
 //                expert histogram, the prefix sums, the stable grouping of the
 //                pairs, the tile lists and the work items, all in LDS.
@@ -19,36 +19,43 @@ namespace moe {
 
 constexpr int RS_RING = 8;  // K steps in flight per wave
 
-__global__ __launch_bounds__(256) void router_small(const uint16_t *__restrict__ x,
-                                                    const uint16_t *__restrict__ wr,
-                                                    const float *__restrict__ bias,
-                                                    float *__restrict__ logits, int T, int H, int E)
+// RW waves split K in RW equal parts (RW * 32 dividing H); for H = 2048 and
+// RW = 8 every wave's whole share is in flight at once.
+template <int RW>
+__global__ __launch_bounds__(64 * RW) void router_small(const uint16_t *__restrict__ x,
+                                                        const uint16_t *__restrict__ wr,
+                                                        const float *__restrict__ bias,
+                                                        float *__restrict__ logits, int T, int H,
+                                                        int E)
 {
-    __shared__ float red[4][16][17];
+    __shared__ float red[RW][16][17];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
     const int e0 = blockIdx.x * 16;
-    const int kq = H / 4;  // K quarter of this wave (multiple of 32)
+    const int kq = H / RW;  // K share of this wave (multiple of 32)
     const uint16_t *wp = wr + (int64_t)min(e0 + l16, E - 1) * H + wave * kq + lg * 8;
     const uint16_t *xp = x + (int64_t)min(l16, T - 1) * H + wave * kq + lg * 8;
     const int nst = kq / 32;
     uint4 wq[RS_RING], xq[RS_RING];
 #pragma unroll
-    for (int d = 0; d < RS_RING; ++d) {
-        wq[d] = *(const uint4 *)(wp + min(d, nst - 1) * 32);
-        xq[d] = *(const uint4 *)(xp + min(d, nst - 1) * 32);
-    }
+    for (int d = 0; d < RS_RING; ++d)
+        if (d < nst) {
+            wq[d] = *(const uint4 *)(wp + d * 32);
+            xq[d] = *(const uint4 *)(xp + d * 32);
+        }
     floatx4 acc = {0, 0, 0, 0};
     for (int s0 = 0; s0 < nst; s0 += RS_RING) {
 #pragma unroll
         for (int d = 0; d < RS_RING; ++d) {
             const int s = s0 + d;
-            const bf16x8 wf = as_bf16x8(wq[d]), xf = as_bf16x8(xq[d]);
-            const int nx = min(s + RS_RING, nst - 1) * 32;
-            wq[d] = *(const uint4 *)(wp + nx);
-            xq[d] = *(const uint4 *)(xp + nx);
-            if (s < nst)
+            if (s < nst) {
+                const bf16x8 wf = as_bf16x8(wq[d]), xf = as_bf16x8(xq[d]);
+                if (s + RS_RING < nst) {
+                    wq[d] = *(const uint4 *)(wp + (s + RS_RING) * 32);
+                    xq[d] = *(const uint4 *)(xp + (s + RS_RING) * 32);
+                }
                 acc = mfma16(wf, xf, acc);
+            }
         }
     }
     // C[expert 4*lg + i][token l16]
@@ -60,7 +67,10 @@ __global__ __launch_bounds__(256) void router_small(const uint16_t *__restrict__
         const int er = tid >> 4, t = tid & 15;  // 16 experts x 16 tokens
         const int e = e0 + er;
         if (t < T && e < E) {
-            float v = ((red[0][er][t] + red[1][er][t]) + red[2][er][t]) + red[3][er][t];
+            float v = red[0][er][t];
+#pragma unroll
+            for (int w = 1; w < RW; ++w)  // in wave order: a fixed sum
+                v += red[w][er][t];
             logits[(int64_t)t * E + e] = v + (bias ? bias[e] : 0.0f);
         }
     }
@@ -113,8 +123,9 @@ __global__ __launch_bounds__(1024) void route_small(
         s_warp[wv] = iv;
     __syncthreads();
     int pv = 0;
-    for (int q = 0; q < wv; ++q)
-        pv += s_warp[q];
+#pragma unroll
+    for (int q = 0; q < 16; ++q)  // all 16 reads in flight together
+        pv += q < wv ? s_warp[q] : 0;
     const int ex = pv + iv - v;
     const int exc = ex & 0x7FF, exa = (ex >> 11) & 0x3FF, exb = (ex >> 21) & 0x3FF;
     if (tid < G) {
@@ -176,9 +187,12 @@ bool route_small_ok(int T, int k, int E) { return T <= 16 && T * k <= 256 && E <
 
 void launch_router_small(const RouterArgs &r, hipStream_t st)
 {
-    if (r.act == ACT_BF16 && r.E % 16 == 0 && r.H % 128 == 0)
-        router_small<<<r.E / 16, 256, 0, st>>>((const uint16_t *)r.x, (const uint16_t *)r.wr,
-                                               r.bias, r.logits, r.T, r.H, r.E);
+    if (r.act == ACT_BF16 && r.E % 16 == 0 && r.H % 256 == 0)
+        router_small<8><<<r.E / 16, 512, 0, st>>>((const uint16_t *)r.x, (const uint16_t *)r.wr,
+                                                  r.bias, r.logits, r.T, r.H, r.E);
+    else if (r.act == ACT_BF16 && r.E % 16 == 0 && r.H % 128 == 0)
+        router_small<4><<<r.E / 16, 256, 0, st>>>((const uint16_t *)r.x, (const uint16_t *)r.wr,
+                                                  r.bias, r.logits, r.T, r.H, r.E);
     else
         launch_router_logits(r, st);
 }
