@@ -20,6 +20,7 @@ struct RouterArgs {
     float *logits;        // [T, E] workspace
     int32_t *idx;         // [T, k]
     float *w;             // [T, k]
+    int32_t *ticket;      // route_small's counter, cleared by router_small (or null)
     int T, H, E, k, act;
 };
 void launch_router(const RouterArgs &a, hipStream_t st);         // logits + top-k
@@ -52,7 +53,8 @@ void launch_permute(const PermuteArgs &a, hipStream_t st);
 
 // Short passes (route_small.hip): router logits, top-k and the whole
 // permutation in two launches.
-bool route_small_ok(int T, int k, int E);
+bool route_small_ok(int T, int k, int E, int H, int act);
+int router_small_rw(int E, int H, int act);  // waves of router_small, 0 if it does not apply
 void launch_router_small(const RouterArgs &r, hipStream_t st);  // logits only
 void launch_route_small(const RouterArgs &r, const PermuteArgs &a, hipStream_t st);  // top-k + permutation
 

@@ -262,7 +262,8 @@ int route_pass(const moe_shape_t *s, const moe_weights_t *w, const void *x, int 
     r.E = s->E;
     r.k = s->top_k;
     r.act = s->act_dtype == MOE_BF16 ? moe::ACT_BF16 : moe::ACT_F32;
-    const bool small = moe::route_small_ok(Tc, s->top_k, s->E);
+    const bool small = moe::route_small_ok(Tc, s->top_k, s->E, s->H, r.act);
+    r.ticket = small ? (int32_t *)(ws + L.blk) : nullptr;
     {
         StageScope sc(0, st);
         if (small)

@@ -1,12 +1,19 @@
-// Router and permutation for short passes (decode and verify shapes, at most
-// 16 tokens and 256 (token, slot) pairs): two launches instead of seven.
+// Router and permutation for short passes (decode, verify and small chunks:
+// at most 128 tokens and 1024 (token, slot) pairs): two launches instead of
+// seven.
 //
-//  router_small: logits of <= 16 tokens; each workgroup owns 16 experts and
-//                its 8 (or 4) waves split K, then add their partial sums in
-//                a fixed order (deterministic).
-//  route_small:  one workgroup: top-k and weights of every token, then the
-//                expert histogram, the prefix sums, the stable grouping of the
-//                pairs, the tile lists and the work items, all in LDS.
+//  router_small: logits; a workgroup owns 16 experts x 16 tokens and its 8
+//                waves split K in eight equal parts, then add their partial
+//                sums in wave order (deterministic).  The long-pass router
+//                GEMM keeps the same eight partial sums and adds them in the
+//                same order, so both give the same bits.
+//  route_small:  one workgroup per 4 tokens (16 if they are all) does their
+//                top-k and weights;
+//                the last workgroup to finish (a ticket counter that
+//                router_small clears) then builds the expert histogram, the
+//                prefix sums, the stable grouping of the pairs, the tile
+//                lists and the work items, all in LDS.  With one workgroup
+//                there is no ticket.
 //
 // Pages: "DeepSeek V4.1F Q4 with native DSpark MTP" (decode paragraph: the
 // time went to hundreds of small dispatches per token, and the router was
@@ -20,21 +27,25 @@ namespace moe {
 constexpr int RS_RING = 8;  // K steps in flight per wave
 
 // RW waves split K in RW equal parts (RW * 32 dividing H); for H = 2048 and
-// RW = 8 every wave's whole share is in flight at once.
+// RW = 8 every wave's whole share is in flight at once.  Grid: (E / 16,
+// ceil(T / 16)).
 template <int RW>
 __global__ __launch_bounds__(64 * RW) void router_small(const uint16_t *__restrict__ x,
                                                         const uint16_t *__restrict__ wr,
                                                         const float *__restrict__ bias,
-                                                        float *__restrict__ logits, int T, int H,
+                                                        float *__restrict__ logits,
+                                                        int32_t *__restrict__ ticket, int T, int H,
                                                         int E)
 {
     __shared__ float red[RW][16][17];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
-    const int e0 = blockIdx.x * 16;
+    const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
+    if (ticket && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0)
+        *ticket = 0;  // the route kernel after this one counts on it
     const int kq = H / RW;  // K share of this wave (multiple of 32)
     const uint16_t *wp = wr + (int64_t)min(e0 + l16, E - 1) * H + wave * kq + lg * 8;
-    const uint16_t *xp = x + (int64_t)min(l16, T - 1) * H + wave * kq + lg * 8;
+    const uint16_t *xp = x + (int64_t)min(t0 + l16, T - 1) * H + wave * kq + lg * 8;
     const int nst = kq / 32;
     uint4 wq[RS_RING], xq[RS_RING];
 #pragma unroll
@@ -64,93 +75,169 @@ __global__ __launch_bounds__(64 * RW) void router_small(const uint16_t *__restri
         red[wave][4 * lg + i][l16] = acc[i];
     __syncthreads();
     if (tid < 256) {
-        const int er = tid >> 4, t = tid & 15;  // 16 experts x 16 tokens
+        const int er = tid >> 4, t = t0 + (tid & 15);  // 16 experts x 16 tokens
         const int e = e0 + er;
         if (t < T && e < E) {
-            float v = red[0][er][t];
+            float v = red[0][er][tid & 15];
 #pragma unroll
             for (int w = 1; w < RW; ++w)  // in wave order: a fixed sum
-                v += red[w][er][t];
+                v += red[w][er][tid & 15];
             logits[(int64_t)t * E + e] = v + (bias ? bias[e] : 0.0f);
         }
     }
 }
 
+// Inclusive prefix sum over the wave: DPP row shifts within each 16-lane
+// row, then the row broadcasts carry the totals of the rows before.
+__device__ __forceinline__ int wave_scan_add(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
+    return v;
+}
+
+// Tokens whose top-k one route workgroup takes: 16 when it is the only one,
+// else 4 (one wave per SIMD: the selection is a chain of wave reductions).
+constexpr int route_tpw(int T) { return T <= 16 ? 16 : 4; }
+
 template <int PER>
 __global__ __launch_bounds__(1024) void route_small(
     const float *__restrict__ logits, int32_t *__restrict__ idx, float *__restrict__ w, int T,
-    int E, int k, int shared, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ row_src, int32_t *__restrict__ row_tok, int32_t *__restrict__ row_of,
-    Tile *__restrict__ tiles_a, int32_t *__restrict__ ntiles_a, Tile *__restrict__ tiles_b,
-    int32_t *__restrict__ ntiles_b, int bm_a, int bm_b, int4 *__restrict__ items_a, int ntn_a,
-    int wrows_a, int4 *__restrict__ items_b, int ntn_b, int wrows_b)
+    int E, int k, int shared, int32_t *__restrict__ ticket, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ row_src, int32_t *__restrict__ row_tok,
+    int32_t *__restrict__ row_of, Tile *__restrict__ tiles_a, int32_t *__restrict__ ntiles_a,
+    Tile *__restrict__ tiles_b, int32_t *__restrict__ ntiles_b, int bm_a, int bm_b,
+    int4 *__restrict__ items_a, int ntn_a, int wrows_a, int4 *__restrict__ items_b, int ntn_b,
+    int wrows_b)
 {
-    __shared__ int s_idx[256];
+    __shared__ int s_idx[1024];
     __shared__ int s_cnt[1025], s_off[1025], s_ta[1025], s_tb[1025];
-    __shared__ int s_warp[16];
-    __shared__ TopkLds s_topk[16];
+    // per wave and group: the wave's pairs of the group, then the pairs of
+    // the group in the waves before it
+    __shared__ uint16_t s_wc[16][1024];
+    __shared__ int s_warp[2][16];
+    __shared__ int s_last;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int P = T * k;
     const int G = E + (shared ? 1 : 0);
+    const bool one = gridDim.x == 1;
 
-    // 1. top-k and weights, one wave per token
-    for (int g = tid; g < G; g += 1024)
-        s_cnt[g] = g < E ? 0 : T;
-    for (int t = wv; t < T; t += 16)
+    // 1. top-k and weights of this workgroup's tokens, one wave per token
+    const int tpw = route_tpw(T);
+    const int t = blockIdx.x * tpw + wv;
+    if (wv < tpw && t < T)
         wave_topk<PER>(logits + (int64_t)t * E, E, k, idx + (int64_t)t * k, w + (int64_t)t * k,
-                       s_idx + t * k, s_topk + wv);
+                       one ? s_idx + t * k : nullptr);
+    if (!one) {
+        // The last workgroup through here does the rest.  The barrier orders
+        // the workgroup's stores before thread 0's device-scope release, which
+        // publishes them all before the ticket is taken.
+        __syncthreads();
+        if (tid == 0) {
+            __threadfence();
+            s_last = atomicAdd(ticket, 1) == (int)gridDim.x - 1;
+            __threadfence();
+        }
+        __syncthreads();
+        if (!s_last)
+            return;
+        if (tid < P)
+            s_idx[tid] = __hip_atomic_load(idx + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const int nwv = (P + 63) / 64;  // waves holding pairs
+    if (tid < G)
+        for (int q = 0; q < nwv; ++q)
+            s_wc[q][tid] = 0;
     __syncthreads();
 
-    // 2. pairs per group (integer counts: the order of the additions is immaterial)
-    if (tid < P)
-        atomicAdd(&s_cnt[s_idx[tid]], 1);
+    // 2. rank of each pair among the earlier pairs of its wave with the same
+    // expert: the lanes holding the same expert are found bit by bit of the
+    // expert index (a ballot per bit); the last such lane records the wave's
+    // count (one writer)
+    const int e = tid < P ? s_idx[tid] : -1;
+    int rank = 0;
+    if (wv < nwv) {  // uniform
+        uint64_t same = __ballot(e >= 0);
+        for (int b = 0; (E - 1) >> b; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t ones = __ballot(bit);
+            same &= bit ? ones : ~ones;
+        }
+        const uint64_t below = (1ull << lane) - 1;
+        rank = __popcll(same & below);
+        if (e >= 0 && (same >> lane) == 1ull)  // no later lane of the expert
+            s_wc[wv][e] = (uint16_t)(rank + 1);
+    }
     __syncthreads();
 
-    // 3. exclusive prefix sums of the rows and of the tiles of both lists, in
-    // one scan of packed fields (rows < 2^11, tiles < 2^10: at most 272 rows)
-    const int c = tid < G ? s_cnt[tid] : 0;
-    const int va = tid < G ? (c + bm_a - 1) / bm_a : 0;
-    const int vb = tid < G ? (c + bm_b - 1) / bm_b : 0;
-    const int v = c | (va << 11) | (vb << 21);
-    int iv = v;
+    // 3. pairs per group and, per wave, the group's pairs in earlier waves;
+    // 4. exclusive prefix sums of the rows and of the tiles of both lists
+    // (two packed scans: rows and tiles a in 16-bit fields, tiles b).  Only
+    // the waves holding groups take part.
+    const int ngw = (G + 63) / 64;
+    int c = 0, va = 0, vb = 0, i1 = 0, i2 = 0;
+    if (wv < ngw) {  // uniform
+        if (tid < E) {
+            int n[16];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(iv, off);
-        if (lane >= off)
-            iv += t;
-    }
-    if (lane == 63)
-        s_warp[wv] = iv;
-    __syncthreads();
-    int pv = 0;
+            for (int q = 0; q < 16; ++q)  // all reads in flight together
+                n[q] = q < nwv ? s_wc[q][tid] : 0;
 #pragma unroll
-    for (int q = 0; q < 16; ++q)  // all 16 reads in flight together
-        pv += q < wv ? s_warp[q] : 0;
-    const int ex = pv + iv - v;
-    const int exc = ex & 0x7FF, exa = (ex >> 11) & 0x3FF, exb = (ex >> 21) & 0x3FF;
-    if (tid < G) {
-        counts[tid] = c;
-        offsets[tid] = exc;
-        s_off[tid] = exc;
-        s_ta[tid] = exa;
-        s_tb[tid] = exb;
+            for (int q = 0; q < 16; ++q) {
+                if (q < nwv)
+                    s_wc[q][tid] = (uint16_t)c;
+                c += n[q];
+            }
+        } else if (tid < G) {
+            c = T;  // the shared expert: every token
+        }
+        if (tid < G) {
+            s_cnt[tid] = c;
+            va = (c + bm_a - 1) / bm_a;
+            vb = (c + bm_b - 1) / bm_b;
+        }
+        i1 = wave_scan_add(c | (va << 16));
+        i2 = wave_scan_add(vb);
+        if (lane == 63) {
+            s_warp[0][wv] = i1;
+            s_warp[1][wv] = i2;
+        }
     }
-    if (tid == G - 1) {
-        offsets[G] = exc + c;
-        *ntiles_a = exa + va;
-        *ntiles_b = exb + vb;
+    __syncthreads();
+    if (wv < ngw) {
+        int p1 = 0, p2 = 0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {  // all reads in flight together
+            const bool in = q < wv;
+            p1 += in ? s_warp[0][q] : 0;
+            p2 += in ? s_warp[1][q] : 0;
+        }
+        const int ex1 = p1 + i1 - (c | (va << 16)), exb = p2 + i2 - vb;
+        const int exc = ex1 & 0xFFFF, exa = ex1 >> 16;
+        if (tid < G) {
+            counts[tid] = c;
+            offsets[tid] = exc;
+            s_off[tid] = exc;
+            s_ta[tid] = exa;
+            s_tb[tid] = exb;
+        }
+        if (tid == G - 1) {
+            offsets[G] = exc + c;
+            *ntiles_a = exa + va;
+            *ntiles_b = exb + vb;
+        }
+        if (!shared && tid == 0)
+            offsets[E + 1] = P;
     }
-    if (!shared && tid == 0)
-        offsets[E + 1] = P;
     __syncthreads();
 
-    // 4. stable grouping: rank of pair p among earlier pairs of its expert
-    if (tid < P) {
-        const int e = s_idx[tid];
-        int rank = 0;
-        for (int q = 0; q < tid; ++q)
-            rank += s_idx[q] == e;
-        const int pos = s_off[e] + rank;
+    // 5. grouped position of each pair: stable (t, j) order within its expert
+    if (e >= 0) {
+        const int pos = s_off[e] + s_wc[wv][e] + rank;
         row_src[pos] = tid;
         row_tok[pos] = tid / k;
         row_of[tid] = pos;
@@ -160,7 +247,7 @@ __global__ __launch_bounds__(1024) void route_small(
         row_tok[P + tid] = tid;
     }
 
-    // 5. tile lists and work items, one thread per group
+    // 6. tile lists and work items, one thread per group
     for (int g = tid; g < G; g += 1024) {
         const int cg = s_cnt[g], og = s_off[g];
         if (cg == 0)
@@ -183,28 +270,47 @@ __global__ __launch_bounds__(1024) void route_small(
     }
 }
 
-bool route_small_ok(int T, int k, int E) { return T <= 16 && T * k <= 256 && E <= 1023; }
+bool route_small_ok(int T, int k, int E, int H, int act)
+{
+    if (T > 128 || T * k > 1024 || k > 16 || E > 1023)
+        return false;
+    // more than one route workgroup needs the ticket that router_small clears
+    return T <= 16 || router_small_rw(E, H, act) > 0;
+}
+
+int router_small_rw(int E, int H, int act)
+{
+    if (act != ACT_BF16 || E % 16 != 0)
+        return 0;
+    return H % 256 == 0 ? 8 : H % 128 == 0 ? 4 : 0;
+}
 
 void launch_router_small(const RouterArgs &r, hipStream_t st)
 {
-    if (r.act == ACT_BF16 && r.E % 16 == 0 && r.H % 256 == 0)
-        router_small<8><<<r.E / 16, 512, 0, st>>>((const uint16_t *)r.x, (const uint16_t *)r.wr,
-                                                  r.bias, r.logits, r.T, r.H, r.E);
-    else if (r.act == ACT_BF16 && r.E % 16 == 0 && r.H % 128 == 0)
-        router_small<4><<<r.E / 16, 256, 0, st>>>((const uint16_t *)r.x, (const uint16_t *)r.wr,
-                                                  r.bias, r.logits, r.T, r.H, r.E);
-    else
-        launch_router_logits(r, st);
+    const dim3 grid(r.E / 16, (r.T + 15) / 16);
+    switch (router_small_rw(r.E, r.H, r.act)) {
+    case 8:
+        router_small<8><<<grid, 512, 0, st>>>((const uint16_t *)r.x, (const uint16_t *)r.wr, r.bias,
+                                              r.logits, r.ticket, r.T, r.H, r.E);
+        break;
+    case 4:
+        router_small<4><<<grid, 256, 0, st>>>((const uint16_t *)r.x, (const uint16_t *)r.wr, r.bias,
+                                              r.logits, r.ticket, r.T, r.H, r.E);
+        break;
+    default:
+        launch_router_logits(r, st);  // one route workgroup only: no ticket
+        break;
+    }
 }
 
 template <int PER>
 static void route_small_per(const RouterArgs &r, const PermuteArgs &a, hipStream_t st)
 {
-    route_small<PER><<<1, 1024, 0, st>>>(r.logits, r.idx, r.w, r.T, r.E, r.k, a.shared, a.counts,
-                                         a.offsets, a.row_src, a.row_tok, a.row_of, a.tiles_a,
-                                         a.ntiles_a, a.tiles_b, a.ntiles_b, a.bm_a, a.bm_b,
-                                         a.items_a, a.ntn_a, a.wrows_a, a.items_b, a.ntn_b,
-                                         a.wrows_b);
+    const int tpw = route_tpw(r.T);
+    route_small<PER><<<(r.T + tpw - 1) / tpw, 1024, 0, st>>>(
+        r.logits, r.idx, r.w, r.T, r.E, r.k, a.shared, r.ticket, a.counts, a.offsets, a.row_src,
+        a.row_tok, a.row_of, a.tiles_a, a.ntiles_a, a.tiles_b, a.ntiles_b, a.bm_a, a.bm_b,
+        a.items_a, a.ntn_a, a.wrows_a, a.items_b, a.ntn_b, a.wrows_b);
 }
 
 void launch_route_small(const RouterArgs &r, const PermuteArgs &a, hipStream_t st)

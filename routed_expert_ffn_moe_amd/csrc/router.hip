@@ -67,8 +67,9 @@ __global__ __launch_bounds__(64 * WN) void router_logits_bf16(
 // it runs at the pace its loads arrive: the chunk queue and the ring keep
 // about 100 KB per workgroup in flight.  The MFMA takes the expert rows as
 // its A operand, so a lane ends up with 4 consecutive experts of one token
-// and stores them as one 16-byte word.  Every logit is the sequential sum
-// over K in 32-wide MFMA steps, whatever RT and the grid are.
+// and stores them as one 16-byte word.  Every logit is the same sum whatever
+// RT and the grid are: eight sequential chains over consecutive eighths of
+// K in 32-wide MFMA steps, added in K order.
 constexpr int RKC = 128;        // K chunk staged in LDS
 constexpr int RLD = RKC + 8;    // padded LDS row (bf16)
 constexpr int RTL = 4;          // token chunks in flight in registers
@@ -86,7 +87,14 @@ __global__ __launch_bounds__(256, 1) void router_gemm(const uint16_t *__restrict
     __shared__ __attribute__((aligned(16))) uint16_t sX[2][RT * RLD];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
-    const int t0 = blockIdx.y * RT, e0 = blockIdx.x * 64 + wave * 16;
+    // Workgroups are dealt to the 8 XCDs in turn; the grid's tiles are
+    // renumbered so that each XCD takes a contiguous run of them, token block
+    // by token block: the expert blocks that share a token block read its
+    // rows from one L2.
+    const int nbx = E / 64, n = gridDim.x;
+    const int b = blockIdx.x;
+    const int L = (n & 7) ? b : (b & 7) * (n >> 3) + (b >> 3);
+    const int t0 = (L / nbx) * RT, e0 = (L % nbx) * 64 + wave * 16;
     // expert row of this lane: MFMA row l16 -> expert e0 + l16
     const uint16_t *wp = wr + (int64_t)min(e0 + l16, E - 1) * H + lg * 8;
     int xo[XCH], so[XCH];
@@ -114,10 +122,16 @@ __global__ __launch_bounds__(256, 1) void router_gemm(const uint16_t *__restrict
                             *(const uint4 *)(x + xo[i] + min(q, nchunks - 1) * RKC));
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    floatx4 acc[MB];
+    floatx4 acc[MB], tot[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-        acc[mb] = floatx4{0, 0, 0, 0};
+        acc[mb] = tot[mb] = floatx4{0, 0, 0, 0};
+    // K in eight equal segments (H % 256 == 0): each segment's chain of
+    // MFMAs starts from zero and the segment sums are added in K order, the
+    // same arithmetic as the short-pass router's eight waves.
+    const int sps = nsteps / 8;
+    int left = sps;
+    bool first = true;
     int buf = 0;
     for (int c = 0; c < nchunks; c += RTL) {
 #pragma unroll
@@ -135,6 +149,15 @@ __global__ __launch_bounds__(256, 1) void router_gemm(const uint16_t *__restrict
                     const bf16x8 tf =
                         as_bf16x8(*(const uint4 *)(Xs + (mb * 16 + l16) * RLD + s4 * 32 + lg * 8));
                     acc[mb] = mfma16(wf, tf, acc[mb]);
+                }
+                if (--left == 0) {  // end of a K segment (uniform)
+                    left = sps;
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        tot[mb] = first ? acc[mb] : tot[mb] + acc[mb];
+                        acc[mb] = floatx4{0, 0, 0, 0};
+                    }
+                    first = false;
                 }
             }
             // chunk cc + 1 into the other buffer, then its slot takes chunk
@@ -163,7 +186,7 @@ __global__ __launch_bounds__(256, 1) void router_gemm(const uint16_t *__restrict
         const int t = t0 + mb * 16 + l16;
         if (t < T)
             *(float4 *)(logits + (int64_t)t * E + e) =
-                float4{acc[mb][0] + bv.x, acc[mb][1] + bv.y, acc[mb][2] + bv.z, acc[mb][3] + bv.w};
+                float4{tot[mb][0] + bv.x, tot[mb][1] + bv.y, tot[mb][2] + bv.z, tot[mb][3] + bv.w};
     }
 }
 
@@ -190,13 +213,12 @@ __global__ __launch_bounds__(256) void router_topk(
     const float *__restrict__ logits, int32_t *__restrict__ idx, float *__restrict__ w,
     int T, int E, int k)
 {
-    __shared__ TopkLds sh[4];
     const int wv = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wv;
     if (t >= T)
         return;
     wave_topk<PER>(logits + (int64_t)t * E, E, k, idx + (int64_t)t * k, w + (int64_t)t * k,
-                   nullptr, sh + wv);
+                   nullptr);
 }
 
 void launch_router_logits(const RouterArgs &a, hipStream_t st)
@@ -206,11 +228,11 @@ void launch_router_logits(const RouterArgs &a, hipStream_t st)
     if (a.act == ACT_BF16 && a.T > 16 && a.E % 64 == 0 && a.H % (RKC * RTL) == 0) {
         // 64 tokens per workgroup for long chunks, 32 otherwise (more workgroups)
         if (a.T >= 4096) {
-            dim3 grid(a.E / 64, (a.T + 63) / 64);
+            const unsigned grid = (unsigned)(a.E / 64 * ((a.T + 63) / 64));
             router_gemm<64><<<grid, 256, 0, st>>>((const uint16_t *)a.x, (const uint16_t *)a.wr,
                                                  a.bias, a.logits, a.T, a.H, a.E);
         } else {
-            dim3 grid(a.E / 64, (a.T + 31) / 32);
+            const unsigned grid = (unsigned)(a.E / 64 * ((a.T + 31) / 32));
             router_gemm<32><<<grid, 256, 0, st>>>((const uint16_t *)a.x, (const uint16_t *)a.wr,
                                                  a.bias, a.logits, a.T, a.H, a.E);
         }

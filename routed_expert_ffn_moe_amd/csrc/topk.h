@@ -6,109 +6,122 @@
 
 namespace moe {
 
-// (value, index) order of the selection: larger logit first, equal logits by
-// lower expert index.
-__device__ __forceinline__ bool better(float va, int ia, float vb, int ib)
-{
-    return va > vb || (va == vb && ia < ib);
-}
-
-// Unsigned key with the order of the floats (NaN is taken as -inf).
+// Unsigned key with the order of the floats: larger key, larger logit.  NaN
+// is taken as -inf and -0 as +0, so equal keys are equal logits.
 __device__ __forceinline__ uint32_t order_key(float x)
 {
-    const uint32_t u = __float_as_uint(x != x ? -INFINITY : x);
+    const uint32_t u = __float_as_uint(x != x ? -INFINITY : x + 0.0f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// LDS scratch of one wave: the k selected (logit, expert) pairs in selection
-// order, then the logits in rank order.
-struct TopkLds {
-    float v[16];
-    int e[16];
-    float s[16];
-};
-
-// Makes one wave's LDS writes visible to its other lanes.
-__device__ __forceinline__ void wave_sync()
+// The logit of a key (the canonical one: never NaN or -0).
+__device__ __forceinline__ float key_value(uint32_t k)
 {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// Lane l holds logits l, l+64, ... (E <= 64*PER).  The k-th largest key is
-// found bit by bit from the top (a radix select: 32 wave-wide counts, no
-// data exchange between lanes), the keys above it and the lowest-index ties
-// at it form the selection, and each selected pair's rank is its number of
-// better pairs.  Weights are the softmax over the selected logits (the full
-// softmax renormalised), summed in rank order.  NaN logits rank last.
-// Writes idx[0..k) and w[0..k) (in rank order), and sidx[0..k) if given.
+// Largest value over the wave, in every lane: prefix maxima within each
+// 16-lane row by DPP row shifts, the rows joined by the row broadcasts, and
+// lane 63 read back.  Lanes a shift reaches past keep their own value.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    const int x = (int)v;
+    int m = x;
+    m = (int)max((uint32_t)m, (uint32_t)__builtin_amdgcn_update_dpp(m, m, 0x111, 0xf, 0xf, false));
+    m = (int)max((uint32_t)m, (uint32_t)__builtin_amdgcn_update_dpp(m, m, 0x112, 0xf, 0xf, false));
+    m = (int)max((uint32_t)m, (uint32_t)__builtin_amdgcn_update_dpp(m, m, 0x114, 0xf, 0xf, false));
+    m = (int)max((uint32_t)m, (uint32_t)__builtin_amdgcn_update_dpp(m, m, 0x118, 0xf, 0xf, false));
+    m = (int)max((uint32_t)m, (uint32_t)__builtin_amdgcn_update_dpp(m, m, 0x142, 0xa, 0xf, false));
+    m = (int)max((uint32_t)m, (uint32_t)__builtin_amdgcn_update_dpp(m, m, 0x143, 0xc, 0xf, false));
+    return (uint32_t)__builtin_amdgcn_readlane(m, 63);
+}
+
+// Smallest value over the wave (same pattern).
+__device__ __forceinline__ int wave_min_i32(int v)
+{
+    int m = v;
+    m = min(m, __builtin_amdgcn_update_dpp(m, m, 0x111, 0xf, 0xf, false));
+    m = min(m, __builtin_amdgcn_update_dpp(m, m, 0x112, 0xf, 0xf, false));
+    m = min(m, __builtin_amdgcn_update_dpp(m, m, 0x114, 0xf, 0xf, false));
+    m = min(m, __builtin_amdgcn_update_dpp(m, m, 0x118, 0xf, 0xf, false));
+    m = min(m, __builtin_amdgcn_update_dpp(m, m, 0x142, 0xa, 0xf, false));
+    m = min(m, __builtin_amdgcn_update_dpp(m, m, 0x143, 0xc, 0xf, false));
+    return __builtin_amdgcn_readlane(m, 63);
+}
+
+// Top-k of one token's router logits and their weights, computed by one
+// wave.  Lane l holds logits l, l+64, ... (E <= 64*PER), sorted once into
+// descending order.  k rounds each take the best remaining (logit, expert)
+// pair of the wave, the head of one lane's list: larger logit first, equal
+// logits by lower expert index; NaN ranks as -inf.  So the pairs come out in
+// rank order, and the weights are the softmax over the selected logits (the
+// full softmax renormalised), summed in rank order.
+// Writes idx[0..k) and w[0..k) in rank order, and sidx[0..k) if given.
 template <int PER>
 __device__ __forceinline__ void wave_topk(const float *__restrict__ lrow, int E, int k,
                                           int32_t *__restrict__ idx, float *__restrict__ w,
-                                          int *sidx, TopkLds *sh)
+                                          int *sidx)
 {
     const int lane = threadIdx.x & 63;
-    float val[PER];
-    uint32_t key[PER];  // 0 for the slots past E: below every logit's key
+    uint32_t key[PER];  // 0 for the slots past E: below every logit
+    int slot[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int e = lane + 64 * i;
-        const bool ok = e < E;
-        const float x = ok ? lrow[e] : -INFINITY;
-        val[i] = x != x ? -INFINITY : x;
-        key[i] = ok ? order_key(x) : 0u;
+        key[i] = e < E ? order_key(lrow[e]) : 0u;
+        slot[i] = i;
     }
-    uint32_t thr = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = thr | (1u << bit);
-        int cnt = 0;
+    // this lane's list in selection order (odd-even transposition sort; a
+    // later slot moves ahead only with a strictly larger key)
 #pragma unroll
-        for (int i = 0; i < PER; ++i)
-            cnt += __popcll(__ballot(key[i] >= cand));
-        thr = cnt >= k ? cand : thr;
-    }
-    int gt = 0;
+    for (int r = 0; r < PER; ++r)
 #pragma unroll
-    for (int i = 0; i < PER; ++i)
-        gt += __popcll(__ballot(key[i] > thr));
-    const int need = k - gt;  // ties at the threshold taken by lower index
-    const uint64_t below = (1ull << lane) - 1;
-    int base_eq = 0, base_sel = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const bool eq = key[i] == thr;
-        const uint64_t meq = __ballot(eq);
-        const bool sel = key[i] > thr || (eq && base_eq + __popcll(meq & below) < need);
-        const uint64_t msel = __ballot(sel);
-        if (sel) {
-            const int slot = base_sel + __popcll(msel & below);
-            sh->v[slot] = val[i];
-            sh->e[slot] = lane + 64 * i;
+        for (int i = r & 1; i + 1 < PER; i += 2)
+            if (key[i + 1] > key[i]) {
+                const uint32_t tk = key[i];
+                key[i] = key[i + 1];
+                key[i + 1] = tk;
+                const int ts = slot[i];
+                slot[i] = slot[i + 1];
+                slot[i + 1] = ts;
+            }
+    int my_e = 0;
+    uint32_t my_k = 0;
+    for (int r = 0; r < k; ++r) {
+        const uint32_t M = wave_max_u32(key[0]);
+        const uint64_t tie = __ballot(key[0] == M);
+        int wl;
+        if (__popcll(tie) == 1) {  // uniform
+            wl = __ffsll((unsigned long long)tie) - 1;
+        } else {  // equal logits: the lowest expert index among the heads
+            const int em = wave_min_i32(key[0] == M ? lane + 64 * slot[0] : 0x7FFFFFFF);
+            wl = em & 63;
         }
-        base_eq += __popcll(meq);
-        base_sel += __popcll(msel);
+        const int er = wl + 64 * __builtin_amdgcn_readlane(slot[0], wl);
+        if (lane == r) {
+            my_e = er;
+            my_k = M;
+        }
+        if (lane == wl) {  // the owner's list moves up
+#pragma unroll
+            for (int i = 0; i + 1 < PER; ++i) {
+                key[i] = key[i + 1];
+                slot[i] = slot[i + 1];
+            }
+            key[PER - 1] = 0u;
+        }
     }
-    wave_sync();
-    float vj = 0.0f;
-    int ej = 0, rank = 0;
+    // softmax of the selected logits; the sum runs in rank order
+    const float mx = key_value(__builtin_amdgcn_readlane(my_k, 0));
+    const float ex = lane < k ? expf(key_value(my_k) - mx) : 0.0f;
+    float z = 0.0f;
+    for (int r = 0; r < k; ++r)
+        z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), r));
     if (lane < k) {
-        vj = sh->v[lane];
-        ej = sh->e[lane];
-        for (int m = 0; m < k; ++m)
-            rank += better(sh->v[m], sh->e[m], vj, ej);
-        sh->s[rank] = vj;
-    }
-    wave_sync();
-    if (lane < k) {
-        const float mx = sh->s[0];
-        float z = 0.0f;
-        for (int j = 0; j < k; ++j)
-            z += expf(sh->s[j] - mx);
-        idx[rank] = ej;
-        w[rank] = expf(vj - mx) / z;
+        idx[lane] = my_e;
+        w[lane] = ex / z;
         if (sidx)
-            sidx[rank] = ej;
+            sidx[lane] = my_e;
     }
 }
 

@@ -80,10 +80,13 @@ def test_forward_parity(name):
     assert err <= hx.TOL[c["w"]], err
 
 
-@pytest.mark.parametrize("name,T", [("c1", None), ("c2", None), ("c1", 9000)])
+@pytest.mark.parametrize("name,T", [("c1", None), ("c1", 16), ("c1", 129), ("c2", None),
+                                    ("c1", 9000)])
 def test_route_and_permutation_bit_exact(name, T):
-    """T=9000 at top-8 is 72,000 pairs: past the one-workgroup permutation,
-    so the multi-block histogram / scan / scatter path runs."""
+    """T=128 and 16: the short-pass kernels with eight and one route
+    workgroups; T=129: the long-pass kernels, one permutation block; T=9000
+    at top-8 is 72,000 pairs: past the one-workgroup permutation, so the
+    multi-block histogram / scan / scatter path runs."""
     say("[route]", name, T)
     c, g = layer(name)
     if T is not None:
@@ -99,10 +102,13 @@ def test_route_and_permutation_bit_exact(name, T):
     assert np.array_equal(row_src.cpu().numpy(), rr)
 
 
-@pytest.mark.parametrize("chunk", [32, 100])
-def test_chunk_invariance(chunk):
-    say("[chunk]", chunk)
-    c, g = layer("c1")
+@pytest.mark.parametrize("name,chunk", [("c1", 32), ("c1", 100), ("c2", 128)])
+def test_chunk_invariance(name, chunk):
+    """Passes of up to 128 tokens take the short-pass router and permutation,
+    longer ones the long-pass kernels; both give the same logits, so the
+    layer's output does not depend on the chunk size."""
+    say("[chunk]", name, chunk)
+    c, g = layer(name)
     x = hx.margin_x(c, g.lay)
     xd = hx.act_torch(x, c["act"], "cuda")
     y0, i0, w0 = g.forward(xd)
@@ -155,6 +161,26 @@ def test_all_tokens_on_the_same_experts():
     tokens = np.arange(0, 300, 7, dtype=np.int32)
     y_ref, _, _ = oracle.forward(hx.oracle_layer(c, lay), x, tokens)
     assert hx.rel_err(hx.y_host(y, "bf16")[tokens], y_ref) <= hx.TOL["bf16"]
+
+
+@pytest.mark.parametrize("T", [5, 100])
+def test_shared_expert_short_passes(T):
+    """The shared expert (group E, every token) through the short-pass
+    routing: one route workgroup (T=5) and several with the ticket (T=100)."""
+    say("[shared short] T =", T)
+    c, g = layer("c3")
+    c = dict(c, T=T, seed=3000 + T)
+    x = hx.margin_x(c, g.lay)
+    y, idx, w = g.forward(hx.act_torch(x, c["act"], "cuda"))
+    idx_h = idx.cpu().numpy()
+    idx_r, _, _ = oracle.route(hx.router_only_layer(c, g.lay), x)
+    assert np.array_equal(idx_h, idx_r)
+    tokens = np.unique(np.linspace(0, T - 1, 6).astype(np.int32))
+    experts = sorted(set(idx_r[tokens].reshape(-1).tolist()))
+    y_ref, _, _ = oracle.forward(hx.oracle_layer(c, g.lay, experts), x, tokens)
+    err = hx.rel_err(hx.y_host(y, c["act"])[tokens], y_ref)
+    say("[shared short] rel err", err)
+    assert err <= hx.TOL[c["w"]], err
 
 
 def test_zero_tokens_is_a_no_op():
