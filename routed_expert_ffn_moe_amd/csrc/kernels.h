@@ -25,6 +25,10 @@ struct RouterArgs {
 };
 void launch_router(const RouterArgs &a, hipStream_t st);         // logits + top-k
 void launch_router_logits(const RouterArgs &a, hipStream_t st);  // logits only
+// Logit planes the router writes for a pass: 8 (partial sums of the eighths
+// of K, when the segmented router applies) or 1; the logits workspace holds
+// that many [T, E] fp32 planes.
+int router_parts(int T, int H, int E, int act);
 
 // Permutation of one pass: counts, offsets and the grouped order of the
 // (t, j) pairs, plus the GEMM tile lists.  Group E is the shared expert

@@ -163,7 +163,9 @@ Layout layout(const moe_shape_t *s, int Tc)
         off = align256(off + bytes);
         return o;
     };
-    L.logits = take((size_t)Tc * s->E * 4);
+    L.logits = take((size_t)Tc * s->E * 4 *
+                    moe::router_parts(Tc, s->H, s->E,
+                                      s->act_dtype == MOE_BF16 ? moe::ACT_BF16 : moe::ACT_F32));
     L.wts = take((size_t)pairs * 4);
     L.blk = take((size_t)std::max(1, moe::permute_blocks((int)pairs)) * s->E * 4);
     L.counts = take((size_t)(s->E + 1) * 4);

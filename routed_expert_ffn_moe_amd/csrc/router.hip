@@ -190,6 +190,95 @@ __global__ __launch_bounds__(256, 1) void router_gemm(const uint16_t *__restrict
     }
 }
 
+// bf16 logits of long passes with K in eight segments across workgroups
+// (H % 2048 == 0, E % 128 == 0): a workgroup owns RT tokens x 128 experts x
+// one eighth of K and writes that segment's partial sums to part[seg][t][e];
+// the top-k kernel adds the eight in K order and then the bias, the same
+// arithmetic as router_gemm and the short-pass router.  Splitting K gives
+// the grid enough workgroups with tiles four times the area of router_gemm's,
+// so far fewer bytes cross from L2 into the CUs.  Per 256-wide pass of the
+// segment, the token rows go to LDS and each wave's 32 expert rows straight
+// into registers, all loads issued before the first MFMA.
+constexpr int SEG_PK = 256;           // K per pass
+constexpr int SEG_LD = SEG_PK + 8;    // padded LDS token row (bf16)
+
+template <int RT>
+__global__ __launch_bounds__(256, 2) void router_seg(const uint16_t *__restrict__ x,
+                                                     const uint16_t *__restrict__ wr,
+                                                     float *__restrict__ part, int T, int H, int E)
+{
+    constexpr int MB = RT / 16;                       // token blocks
+    constexpr int XCH = RT * (SEG_PK / 8) / 256;      // 16-byte token pieces per thread
+    constexpr int NS = SEG_PK / 32;                   // MFMA steps per pass
+    __shared__ __attribute__((aligned(16))) uint16_t sX[RT * SEG_LD];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    // Tiles numbered token block, then segment, then expert block, and dealt
+    // to the XCDs in contiguous runs: the expert blocks of one token block and
+    // segment read its rows from one L2.
+    const int nbe = E / 128, n = gridDim.x, b = blockIdx.x;
+    const int L = (n & 7) ? b : (b & 7) * (n >> 3) + (b >> 3);
+    const int eb = L % nbe, seg = (L / nbe) & 7, tb = L / (nbe * 8);
+    const int t0 = tb * RT, e0 = eb * 128 + wave * 32;
+    const int ks = H / 8;
+    const uint16_t *wp0 = wr + (int64_t)(e0 + l16) * H + seg * ks + lg * 8;
+    const uint16_t *wp1 = wp0 + (int64_t)16 * H;
+    int xo[XCH], so[XCH];
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+        const int q = tid + 256 * i, r = q / (SEG_PK / 8), c8 = q % (SEG_PK / 8);
+        xo[i] = min(t0 + r, T - 1) * H + seg * ks + c8 * 8;
+        so[i] = r * SEG_LD + c8 * 8;
+    }
+    floatx4 acc[2][MB];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+            acc[m][mb] = floatx4{0, 0, 0, 0};
+    for (int k0 = 0; k0 < ks; k0 += SEG_PK) {
+        // held as vector values (registers, never scratch)
+        u32v<NS> wq0, wq1;
+        u32v<XCH> xq;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            vset<NS>(wq0, s, *(const uint4 *)(wp0 + k0 + s * 32));
+            vset<NS>(wq1, s, *(const uint4 *)(wp1 + k0 + s * 32));
+        }
+#pragma unroll
+        for (int i = 0; i < XCH; ++i)
+            vset<XCH>(xq, i, *(const uint4 *)(x + xo[i] + k0));
+        if (k0 > 0)
+            __syncthreads();  // the previous pass's fragments are read
+#pragma unroll
+        for (int i = 0; i < XCH; ++i)
+            *(uint4 *)(&sX[so[i]]) = vget<XCH>(xq, i);
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const bf16x8 w0 = as_bf16x8(vget<NS>(wq0, s)), w1 = as_bf16x8(vget<NS>(wq1, s));
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const bf16x8 tf =
+                    as_bf16x8(*(const uint4 *)(sX + (mb * 16 + l16) * SEG_LD + s * 32 + lg * 8));
+                acc[0][mb] = mfma16(w0, tf, acc[0][mb]);
+                acc[1][mb] = mfma16(w1, tf, acc[1][mb]);
+            }
+        }
+    }
+    // lane: experts e0 + 16m + 4*lg .. +3 of token mb*16 + l16
+    float *dst = part + (int64_t)seg * T * E;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int t = t0 + mb * 16 + l16;
+        if (t < T)
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+                *(float4 *)(dst + (int64_t)t * E + e0 + 16 * m + 4 * lg) =
+                    float4{acc[m][mb][0], acc[m][mb][1], acc[m][mb][2], acc[m][mb][3]};
+    }
+}
+
 // fp32 logits: one thread per (token, expert), plain dot product.
 __global__ __launch_bounds__(256) void router_logits_f32(
     const float *__restrict__ x, const float *__restrict__ wr,
@@ -219,6 +308,39 @@ __global__ __launch_bounds__(256) void router_topk(
         return;
     wave_topk<PER>(logits + (int64_t)t * E, E, k, idx + (int64_t)t * k, w + (int64_t)t * k,
                    nullptr);
+}
+
+// The same from router_seg's eight partial sums: the logit is the sum of the
+// eight in K order, then the bias.
+template <int PER>
+__global__ __launch_bounds__(256) void router_topk_seg(
+    const float *__restrict__ part, const float *__restrict__ bias, int32_t *__restrict__ idx,
+    float *__restrict__ w, int T, int E, int k)
+{
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wv;
+    if (t >= T)
+        return;
+    const int64_t plane = (int64_t)T * E;
+    float p[8][PER];  // all loads in flight together
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = lane + 64 * i;
+            p[s][i] = e < E ? part[s * plane + (int64_t)t * E + e] : 0.0f;
+        }
+    float v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = lane + 64 * i;
+        float a = p[0][i];
+#pragma unroll
+        for (int s = 1; s < 8; ++s)
+            a += p[s][i];
+        v[i] = a + (bias && e < E ? bias[e] : 0.0f);
+    }
+    wave_topk_vals<PER>(v, E, k, idx + (int64_t)t * k, w + (int64_t)t * k, nullptr);
 }
 
 void launch_router_logits(const RouterArgs &a, hipStream_t st)
@@ -253,10 +375,33 @@ void launch_router_logits(const RouterArgs &a, hipStream_t st)
     }
 }
 
+int router_parts(int T, int H, int E, int act)
+{
+    return act == ACT_BF16 && T > 16 && E % 128 == 0 && H % 2048 == 0 ? 8 : 1;
+}
+
 void launch_router(const RouterArgs &a, hipStream_t st)
 {
     if (a.T == 0)
         return;
+    if (router_parts(a.T, a.H, a.E, a.act) == 8) {
+        const int nbe = a.E / 128;
+        if (a.T > 4096)
+            router_seg<128><<<(unsigned)(nbe * 8 * ((a.T + 127) / 128)), 256, 0, st>>>(
+                (const uint16_t *)a.x, (const uint16_t *)a.wr, a.logits, a.T, a.H, a.E);
+        else
+            router_seg<64><<<(unsigned)(nbe * 8 * ((a.T + 63) / 64)), 256, 0, st>>>(
+                (const uint16_t *)a.x, (const uint16_t *)a.wr, a.logits, a.T, a.H, a.E);
+        const unsigned nb = (unsigned)((a.T + 3) / 4);
+        switch (topk_per(a.E)) {
+        case 1: router_topk_seg<1><<<nb, 256, 0, st>>>(a.logits, a.bias, a.idx, a.w, a.T, a.E, a.k); break;
+        case 2: router_topk_seg<2><<<nb, 256, 0, st>>>(a.logits, a.bias, a.idx, a.w, a.T, a.E, a.k); break;
+        case 4: router_topk_seg<4><<<nb, 256, 0, st>>>(a.logits, a.bias, a.idx, a.w, a.T, a.E, a.k); break;
+        case 8: router_topk_seg<8><<<nb, 256, 0, st>>>(a.logits, a.bias, a.idx, a.w, a.T, a.E, a.k); break;
+        default: router_topk_seg<16><<<nb, 256, 0, st>>>(a.logits, a.bias, a.idx, a.w, a.T, a.E, a.k); break;
+        }
+        return;
+    }
     launch_router_logits(a, st);
     const unsigned nb = (unsigned)((a.T + 3) / 4);
     switch (topk_per(a.E)) {

@@ -50,7 +50,7 @@ __device__ __forceinline__ int wave_min_i32(int v)
 }
 
 // Top-k of one token's router logits and their weights, computed by one
-// wave.  Lane l holds logits l, l+64, ... (E <= 64*PER), sorted once into
+// wave.  Lane l holds logits l, l+64, ... (E <= 64*PER) in val, sorted once into
 // descending order.  k rounds each take the best remaining (logit, expert)
 // pair of the wave, the head of one lane's list: larger logit first, equal
 // logits by lower expert index; NaN ranks as -inf.  So the pairs come out in
@@ -58,17 +58,16 @@ __device__ __forceinline__ int wave_min_i32(int v)
 // full softmax renormalised), summed in rank order.
 // Writes idx[0..k) and w[0..k) in rank order, and sidx[0..k) if given.
 template <int PER>
-__device__ __forceinline__ void wave_topk(const float *__restrict__ lrow, int E, int k,
-                                          int32_t *__restrict__ idx, float *__restrict__ w,
-                                          int *sidx)
+__device__ __forceinline__ void wave_topk_vals(const float (&val)[PER], int E, int k,
+                                               int32_t *__restrict__ idx, float *__restrict__ w,
+                                               int *sidx)
 {
     const int lane = threadIdx.x & 63;
     uint32_t key[PER];  // 0 for the slots past E: below every logit
     int slot[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int e = lane + 64 * i;
-        key[i] = e < E ? order_key(lrow[e]) : 0u;
+        key[i] = lane + 64 * i < E ? order_key(val[i]) : 0u;
         slot[i] = i;
     }
     // this lane's list in selection order (odd-even transposition sort; a
@@ -123,6 +122,20 @@ __device__ __forceinline__ void wave_topk(const float *__restrict__ lrow, int E,
         if (sidx)
             sidx[lane] = my_e;
     }
+}
+
+// The same, reading the token's E logits from memory.
+template <int PER>
+__device__ __forceinline__ void wave_topk(const float *__restrict__ lrow, int E, int k,
+                                          int32_t *__restrict__ idx, float *__restrict__ w,
+                                          int *sidx)
+{
+    const int lane = threadIdx.x & 63;
+    float v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+        v[i] = lane + 64 * i < E ? lrow[lane + 64 * i] : 0.0f;
+    wave_topk_vals<PER>(v, E, k, idx, w, sidx);
 }
 
 // Logit slots per lane for E experts: 1, 2, 4, 8 or 16.
