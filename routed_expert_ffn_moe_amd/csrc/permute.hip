@@ -74,6 +74,7 @@ __global__ __launch_bounds__(1024) void permute_scan(
     __shared__ int32_t s_tb[1025];
     __shared__ int32_t s_off[1025];
     __shared__ int32_t s_warp[3][16];
+    __shared__ int32_t s_nt[2];
     __shared__ int32_t s_blk[FUSED_HIST];
     const int tid = threadIdx.x;
     const int G = E + (shared ? 1 : 0);  // groups
@@ -100,10 +101,17 @@ __global__ __launch_bounds__(1024) void permute_scan(
         __syncthreads();
         for (int e = tid; e < E; e += 1024) {
             int run = 0;
-            for (int b = 0; b < nblk; ++b) {
-                const int c = s_blk[b * E + e];
-                s_blk[b * E + e] = run;
-                run += c;
+            for (int b0 = 0; b0 < nblk; b0 += SCH) {
+                int c[SCH];
+#pragma unroll
+                for (int i = 0; i < SCH; ++i)  // all reads in flight together
+                    c[i] = b0 + i < nblk ? s_blk[(b0 + i) * E + e] : 0;
+#pragma unroll
+                for (int i = 0; i < SCH; ++i)
+                    if (b0 + i < nblk) {
+                        s_blk[(b0 + i) * E + e] = run;
+                        run += c[i];
+                    }
             }
             s_cnt[e] = run;
         }
@@ -129,50 +137,53 @@ __global__ __launch_bounds__(1024) void permute_scan(
     if (tid == 0 && shared)
         s_cnt[E] = T;
     __syncthreads();
-    // Exclusive scan over the groups of: row counts, tiles of bm_a, tiles of bm_b.
-    int c = tid < G ? s_cnt[tid] : 0;
-    int va = tid < G ? (c + bm_a - 1) / bm_a : 0;
-    int vb = tid < G ? (c + bm_b - 1) / bm_b : 0;
-    int ic = c, ia = va, ib = vb;  // inclusive scans within the wave
-    const int lane = tid & 63, wv = tid >> 6;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        int tc = __shfl_up(ic, off), ta = __shfl_up(ia, off), tb = __shfl_up(ib, off);
-        if (lane >= off) {
-            ic += tc;
-            ia += ta;
-            ib += tb;
+    // Exclusive scan over the groups of: row counts, tiles of bm_a, tiles of
+    // bm_b (only the waves holding groups take part).
+    const int lane = tid & 63, wv = tid >> 6, ngw = (G + 63) / 64;
+    int c = 0, va = 0, vb = 0, ic = 0, ia = 0, ib = 0;
+    if (wv < ngw) {  // uniform
+        if (tid < G) {
+            c = s_cnt[tid];
+            va = (c + bm_a - 1) / bm_a;
+            vb = (c + bm_b - 1) / bm_b;
+        }
+        ic = wave_scan_add(c);
+        ia = wave_scan_add(va);
+        ib = wave_scan_add(vb);
+        if (lane == 63) {
+            s_warp[0][wv] = ic;
+            s_warp[1][wv] = ia;
+            s_warp[2][wv] = ib;
         }
     }
-    if (lane == 63) {
-        s_warp[0][wv] = ic;
-        s_warp[1][wv] = ia;
-        s_warp[2][wv] = ib;
-    }
     __syncthreads();
-    int pc = 0, pa = 0, pb = 0;
+    if (wv < ngw) {
+        int pc = 0, pa = 0, pb = 0;
 #pragma unroll
-    for (int w = 0; w < 16; ++w) {  // all reads in flight together
-        const bool in = w < wv;
-        pc += in ? s_warp[0][w] : 0;
-        pa += in ? s_warp[1][w] : 0;
-        pb += in ? s_warp[2][w] : 0;
+        for (int w = 0; w < 16; ++w) {  // all reads in flight together
+            const bool in = w < wv;
+            pc += in ? s_warp[0][w] : 0;
+            pa += in ? s_warp[1][w] : 0;
+            pb += in ? s_warp[2][w] : 0;
+        }
+        const int exc = pc + ic - c, exa = pa + ia - va, exb = pb + ib - vb;
+        if (tid < G) {
+            counts[tid] = c;
+            offsets[tid] = exc;
+            s_off[tid] = exc;
+            s_ta[tid] = exa;
+            s_tb[tid] = exb;
+        }
+        if (tid == G - 1) {
+            offsets[G] = exc + c;
+            *ntiles_a = exa + va;
+            *ntiles_b = exb + vb;
+            s_nt[0] = exa + va;
+            s_nt[1] = exb + vb;
+        }
+        if (!shared && tid == 0)
+            offsets[E + 1] = n_pairs;  // empty shared group
     }
-    const int exc = pc + ic - c, exa = pa + ia - va, exb = pb + ib - vb;
-    if (tid < G) {
-        counts[tid] = c;
-        offsets[tid] = exc;
-        s_off[tid] = exc;
-        s_ta[tid] = exa;
-        s_tb[tid] = exb;
-    }
-    if (tid == G - 1) {
-        offsets[G] = exc + c;
-        *ntiles_a = exa + va;
-        *ntiles_b = exb + vb;
-    }
-    if (!shared && tid == 0)
-        offsets[E + 1] = n_pairs;  // empty shared group
     __syncthreads();
     // Per-block start positions inside each expert's range.
     for (int e = tid; e < E; e += 1024) {
@@ -195,34 +206,35 @@ __global__ __launch_bounds__(1024) void permute_scan(
     }
     // Tile lists, and the work items of the streaming GEMMs: expert-major,
     // then column tile, then row tile, so that item lists dealt out in
-    // contiguous runs keep an expert on one XCD.
-    for (int g = tid; g < G; g += 1024) {
-        const int cg = g < E ? s_cnt[g] : T;
-        const int og = s_off[g];
-        const int na = (cg + bm_a - 1) / bm_a, nb = (cg + bm_b - 1) / bm_b;
-        for (int m = 0; m < na; ++m)
-            tiles_a[s_ta[g] + m] = Tile{g, og + m * bm_a};
-        for (int m = 0; m < nb; ++m)
-            tiles_b[s_tb[g] + m] = Tile{g, og + m * bm_b};
+    // contiguous runs keep an expert on one XCD.  One thread per tile; a
+    // tile's group is the last one whose first tile is not after it (groups
+    // without rows take no tiles).
+    const int nta = s_nt[0], ntb = s_nt[1];
+    for (int i = tid; i < nta + ntb; i += 1024) {
+        const bool a = i < nta;
+        const int j = a ? i : i - nta;
+        const int *st = a ? s_ta : s_tb;
+        int lo = 0, hi = G - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (st[mid] <= j)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        const int g = lo, m = j - st[g];
+        const int cg = g < E ? s_cnt[g] : T, og = s_off[g];
+        const int bm = a ? bm_a : bm_b;
+        const int r0 = og + m * bm, nr = min(bm, cg - m * bm);
+        (a ? tiles_a : tiles_b)[j] = Tile{g, r0};
+        int4 *items = a ? items_a : items_b;
+        if (items) {
+            const int ntn = a ? ntn_a : ntn_b, wrows = a ? wrows_a : wrows_b;
+            const int nt_g = (cg + bm - 1) / bm;  // the group's row tiles
+            for (int nt = 0; nt < ntn; ++nt)
+                items[ntn * st[g] + nt * nt_g + m] = int4{g, r0, nr, nt * wrows};
+        }
     }
-    if (items_a)
-        for (int q = tid; q < G * ntn_a; q += 1024) {
-            const int g = q / ntn_a, nt = q - g * ntn_a;
-            const int cg = g < E ? s_cnt[g] : T, og = s_off[g];
-            const int na = (cg + bm_a - 1) / bm_a;
-            for (int m = 0; m < na; ++m)
-                items_a[ntn_a * s_ta[g] + nt * na + m] =
-                    int4{g, og + m * bm_a, min(bm_a, cg - m * bm_a), nt * wrows_a};
-        }
-    if (items_b)
-        for (int q = tid; q < G * ntn_b; q += 1024) {
-            const int g = q / ntn_b, nt = q - g * ntn_b;
-            const int cg = g < E ? s_cnt[g] : T, og = s_off[g];
-            const int nb = (cg + bm_b - 1) / bm_b;
-            for (int m = 0; m < nb; ++m)
-                items_b[ntn_b * s_tb[g] + nt * nb + m] =
-                    int4{g, og + m * bm_b, min(bm_b, cg - m * bm_b), nt * wrows_b};
-        }
 }
 
 // Stable scatter.  Each of a block's 4 waves walks a quarter of its pairs 64

@@ -87,19 +87,6 @@ __global__ __launch_bounds__(64 * RW) void router_small(const uint16_t *__restri
     }
 }
 
-// Inclusive prefix sum over the wave: DPP row shifts within each 16-lane
-// row, then the row broadcasts carry the totals of the rows before.
-__device__ __forceinline__ int wave_scan_add(int v)
-{
-    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);
-    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);
-    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);
-    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);
-    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
-    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
-    return v;
-}
-
 // Tokens whose top-k one route workgroup takes: 16 when it is the only one,
 // else 4 (one wave per SIMD: the selection is a chain of wave reductions).
 constexpr int route_tpw(int T) { return T <= 16 ? 16 : 4; }
