@@ -21,6 +21,10 @@ struct RouterArgs {
     int32_t *idx;         // [T, k]
     float *w;             // [T, k]
     int32_t *ticket;      // route_small's counter, cleared by router_small (or null)
+    // With hist set, the segmented router also counts the pairs of each
+    // permutation block per expert into hist [nblk, E] (cleared first).
+    int32_t *hist;
+    int nhist;
     int T, H, E, k, act;
 };
 void launch_router(const RouterArgs &a, hipStream_t st);         // logits + top-k
@@ -50,8 +54,10 @@ struct PermuteArgs {
     // column tile, then row tile): {group, first row, rows, first column}.
     int4 *items_a, *items_b;
     int ntn_a, ntn_b, max_tiles_a, max_tiles_b, wrows_a, wrows_b;
+    int hist_done;        // blk already holds the per-block counts (from the router)
     int T, E, k, shared;
 };
+constexpr int PERMUTE_PAIRS_PER_BLOCK = 1024;  // pairs per histogram / scatter block
 int permute_blocks(int n_pairs);  // number of histogram blocks
 void launch_permute(const PermuteArgs &a, hipStream_t st);
 

@@ -266,6 +266,10 @@ int route_pass(const moe_shape_t *s, const moe_weights_t *w, const void *x, int 
     r.act = s->act_dtype == MOE_BF16 ? moe::ACT_BF16 : moe::ACT_F32;
     const bool small = moe::route_small_ok(Tc, s->top_k, s->E, s->H, r.act);
     r.ticket = small ? (int32_t *)(ws + L.blk) : nullptr;
+    // the segmented router counts the permutation's block histogram itself
+    const bool seg = !small && moe::router_parts(Tc, s->H, s->E, r.act) == 8;
+    r.hist = seg ? (int32_t *)(ws + L.blk) : nullptr;
+    r.nhist = moe::permute_blocks(Tc * s->top_k) * s->E;
     {
         StageScope sc(0, st);
         if (small)
@@ -292,6 +296,7 @@ int route_pass(const moe_shape_t *s, const moe_weights_t *w, const void *x, int 
     p.bm_b = L.bm_dc;
     p.items_a = L.ntn_gu ? (int4 *)(ws + L.items_gu) : nullptr;
     p.items_b = L.ntn_dc ? (int4 *)(ws + L.items_dc) : nullptr;
+    p.hist_done = seg ? 1 : 0;
     p.ntn_a = L.ntn_gu;
     p.ntn_b = L.ntn_dc;
     p.max_tiles_a = L.max_tiles_gu;

@@ -18,7 +18,7 @@
 
 namespace moe {
 
-constexpr int PAIRS_PER_BLOCK = 1024;
+constexpr int PAIRS_PER_BLOCK = PERMUTE_PAIRS_PER_BLOCK;
 // Passes whose per-block histograms fit in this many LDS counters build them
 // inside the scan kernel (one launch less).
 constexpr int FUSED_HIST = 8192;
@@ -319,8 +319,8 @@ void launch_permute(const PermuteArgs &a, hipStream_t st)
 {
     const int n_pairs = a.T * a.k;
     const int nblk = permute_blocks(n_pairs);
-    const bool fused = nblk * a.E <= FUSED_HIST;
-    if (nblk > 0 && !fused)
+    const bool fused = !a.hist_done && nblk * a.E <= FUSED_HIST;
+    if (nblk > 0 && !fused && !a.hist_done)
         permute_hist<<<nblk, 256, a.E * sizeof(int32_t), st>>>(a.idx, a.blk, n_pairs, a.E);
     permute_scan<<<1, 1024, 0, st>>>(fused ? a.idx : nullptr, a.blk, a.counts, a.offsets, a.tiles_a, a.ntiles_a, a.tiles_b,
                                      a.ntiles_b, a.bm_a, a.bm_b, nblk, a.E, n_pairs, a.T, a.shared,

@@ -205,7 +205,8 @@ constexpr int SEG_LD = SEG_PK + 8;    // padded LDS token row (bf16)
 template <int RT>
 __global__ __launch_bounds__(256, 2) void router_seg(const uint16_t *__restrict__ x,
                                                      const uint16_t *__restrict__ wr,
-                                                     float *__restrict__ part, int T, int H, int E)
+                                                     float *__restrict__ part, int T, int H, int E,
+                                                     int32_t *__restrict__ hist, int nhist)
 {
     constexpr int MB = RT / 16;                       // token blocks
     constexpr int XCH = RT * (SEG_PK / 8) / 256;      // 16-byte token pieces per thread
@@ -213,6 +214,9 @@ __global__ __launch_bounds__(256, 2) void router_seg(const uint16_t *__restrict_
     __shared__ __attribute__((aligned(16))) uint16_t sX[RT * SEG_LD];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
+    // the block histogram the top-k kernel after this one counts into
+    for (int i = blockIdx.x * 256 + tid; i < nhist; i += gridDim.x * 256)
+        hist[i] = 0;
     // Tiles numbered token block, then segment, then expert block, and dealt
     // to the XCDs in contiguous runs: the expert blocks of one token block and
     // segment read its rows from one L2.
@@ -311,11 +315,13 @@ __global__ __launch_bounds__(256) void router_topk(
 }
 
 // The same from router_seg's eight partial sums: the logit is the sum of the
-// eight in K order, then the bias.
+// eight in K order, then the bias.  With hist given, each selected pair also
+// counts into its permutation block's row of the histogram (integer counts:
+// the order of the atomic additions is immaterial).
 template <int PER>
 __global__ __launch_bounds__(256) void router_topk_seg(
     const float *__restrict__ part, const float *__restrict__ bias, int32_t *__restrict__ idx,
-    float *__restrict__ w, int T, int E, int k)
+    float *__restrict__ w, int T, int E, int k, int32_t *__restrict__ hist)
 {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wv;
@@ -341,6 +347,10 @@ __global__ __launch_bounds__(256) void router_topk_seg(
         v[i] = a + (bias && e < E ? bias[e] : 0.0f);
     }
     wave_topk_vals<PER>(v, E, k, idx + (int64_t)t * k, w + (int64_t)t * k, nullptr);
+    if (hist && lane < k) {
+        const int p = t * k + lane;  // this lane's pair, just written by this lane
+        atomicAdd(&hist[(p / PERMUTE_PAIRS_PER_BLOCK) * E + idx[p]], 1);
+    }
 }
 
 void launch_router_logits(const RouterArgs &a, hipStream_t st)
@@ -388,17 +398,19 @@ void launch_router(const RouterArgs &a, hipStream_t st)
         const int nbe = a.E / 128;
         if (a.T > 4096)
             router_seg<128><<<(unsigned)(nbe * 8 * ((a.T + 127) / 128)), 256, 0, st>>>(
-                (const uint16_t *)a.x, (const uint16_t *)a.wr, a.logits, a.T, a.H, a.E);
+                (const uint16_t *)a.x, (const uint16_t *)a.wr, a.logits, a.T, a.H, a.E, a.hist,
+                a.hist ? a.nhist : 0);
         else
             router_seg<64><<<(unsigned)(nbe * 8 * ((a.T + 63) / 64)), 256, 0, st>>>(
-                (const uint16_t *)a.x, (const uint16_t *)a.wr, a.logits, a.T, a.H, a.E);
+                (const uint16_t *)a.x, (const uint16_t *)a.wr, a.logits, a.T, a.H, a.E, a.hist,
+                a.hist ? a.nhist : 0);
         const unsigned nb = (unsigned)((a.T + 3) / 4);
         switch (topk_per(a.E)) {
-        case 1: router_topk_seg<1><<<nb, 256, 0, st>>>(a.logits, a.bias, a.idx, a.w, a.T, a.E, a.k); break;
-        case 2: router_topk_seg<2><<<nb, 256, 0, st>>>(a.logits, a.bias, a.idx, a.w, a.T, a.E, a.k); break;
-        case 4: router_topk_seg<4><<<nb, 256, 0, st>>>(a.logits, a.bias, a.idx, a.w, a.T, a.E, a.k); break;
-        case 8: router_topk_seg<8><<<nb, 256, 0, st>>>(a.logits, a.bias, a.idx, a.w, a.T, a.E, a.k); break;
-        default: router_topk_seg<16><<<nb, 256, 0, st>>>(a.logits, a.bias, a.idx, a.w, a.T, a.E, a.k); break;
+        case 1: router_topk_seg<1><<<nb, 256, 0, st>>>(a.logits, a.bias, a.idx, a.w, a.T, a.E, a.k, a.hist); break;
+        case 2: router_topk_seg<2><<<nb, 256, 0, st>>>(a.logits, a.bias, a.idx, a.w, a.T, a.E, a.k, a.hist); break;
+        case 4: router_topk_seg<4><<<nb, 256, 0, st>>>(a.logits, a.bias, a.idx, a.w, a.T, a.E, a.k, a.hist); break;
+        case 8: router_topk_seg<8><<<nb, 256, 0, st>>>(a.logits, a.bias, a.idx, a.w, a.T, a.E, a.k, a.hist); break;
+        default: router_topk_seg<16><<<nb, 256, 0, st>>>(a.logits, a.bias, a.idx, a.w, a.T, a.E, a.k, a.hist); break;
         }
         return;
     }
