@@ -94,38 +94,6 @@ __device__ __forceinline__ uint4 vget(const u32v<N> &r, int i)
     return uint4{r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]};
 }
 
-// Columns c8 .. c8+7 of combined row t: the k staging rows of token t (the
-// grouped rows row_of[t*k + j]) weighted by its routing weights and summed
-// in slot order j in fp32, plus the shared expert's row (grouped row T*k + t)
-// with weight 1, rounded once to bf16.
-__device__ __forceinline__ uint4 combine_row8(const uint16_t *stage, const int32_t *row_of,
-                                              const float *topk_w, int t, int T, int H, int k,
-                                              int shared, int c8)
-{
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    const int n_rows = k + (shared ? 1 : 0);
-    for (int j = 0; j < n_rows; ++j) {
-        int64_t row;
-        float w;
-        if (j < k) {
-            row = row_of[(int64_t)t * k + j];
-            w = topk_w[(int64_t)t * k + j];
-        } else {
-            row = (int64_t)T * k + t;
-            w = 1.0f;
-        }
-        const uint4 v = *(const uint4 *)(stage + row * H + c8);
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            acc[2 * q] = fmaf(w, bf2f((uint16_t)(w4[q] & 0xFFFF)), acc[2 * q]);
-            acc[2 * q + 1] = fmaf(w, bf2f((uint16_t)(w4[q] >> 16)), acc[2 * q + 1]);
-        }
-    }
-    return uint4{pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3]), pack_bf2(acc[4], acc[5]),
-                 pack_bf2(acc[6], acc[7])};
-}
-
 // Offset (elements) of the 8 K-consecutive elements (n, k .. k+7) of a bf16
 // matrix [N, K] in the packed layout (k a multiple of 8): rows in groups of
 // 32, K in steps of 32, each (group, step) two kilobyte blocks whose lane

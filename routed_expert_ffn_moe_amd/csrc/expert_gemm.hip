@@ -252,7 +252,10 @@ __global__ __launch_bounds__(256) void expert_gemm_f32(GemmF32 p)
 
 // y[t, c] = sum_j w[t*k + j] * stage[row_of[t*k + j], c] (+ stage[T*k + t, c]),
 // fp32 sum in j order, rounded once.  Each thread handles 8 consecutive
-// columns; the staging rows are gathered whole.
+// columns of one token; the row indices and weights of its (at most KM)
+// rows are read first and then all the rows' 16-byte pieces together, so
+// a thread's loads are in flight at once rather than one row at a time.
+template <int KM>
 __global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__ stage,
                                                     const int32_t *__restrict__ row_of,
                                                     const float *__restrict__ topk_w,
@@ -264,8 +267,33 @@ __global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__
     if (i >= (int64_t)T * per_row)
         return;
     const int t = (int)(i / per_row), c8 = (int)(i % per_row) * 8;
-    const uint4 o = combine_row8(stage, row_of, topk_w, t, T, H, k, shared, c8);
-    *(uint4 *)(y + (int64_t)t * H + c8) = o;
+    const int n_rows = k + (shared ? 1 : 0);  // <= KM
+    int64_t row[KM];
+    float w[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+        row[j] = j < k ? row_of[(int64_t)t * k + j] : (int64_t)T * k + t;
+        w[j] = j < k ? topk_w[(int64_t)t * k + j] : 1.0f;
+    }
+    uint4 v[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+        if (j < n_rows)
+            v[j] = *(const uint4 *)(stage + row[j] * H + c8);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+        if (j < n_rows) {
+            const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] = fmaf(w[j], bf2f((uint16_t)(w4[q] & 0xFFFF)), acc[2 * q]);
+                acc[2 * q + 1] = fmaf(w[j], bf2f((uint16_t)(w4[q] >> 16)), acc[2 * q + 1]);
+            }
+        }
+    *(uint4 *)(y + (int64_t)t * H + c8) =
+        uint4{pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3]), pack_bf2(acc[4], acc[5]),
+              pack_bf2(acc[6], acc[7])};
 }
 
 __global__ __launch_bounds__(256) void combine_f32(const float *__restrict__ stage,
@@ -450,8 +478,13 @@ void launch_combine(const CombineArgs &a, hipStream_t st)
         return;
     if (a.act == ACT_BF16) {
         const int64_t n = (int64_t)a.T * (a.H / 8);
-        combine_bf16<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
-            (const uint16_t *)a.stage, a.row_of, a.topk_w, (uint16_t *)a.y, a.T, a.H, a.k, a.shared);
+        const unsigned nb = (unsigned)((n + 255) / 256);
+        if (a.k + (a.shared ? 1 : 0) <= 9)
+            combine_bf16<9><<<nb, 256, 0, st>>>((const uint16_t *)a.stage, a.row_of, a.topk_w,
+                                               (uint16_t *)a.y, a.T, a.H, a.k, a.shared);
+        else
+            combine_bf16<17><<<nb, 256, 0, st>>>((const uint16_t *)a.stage, a.row_of, a.topk_w,
+                                                (uint16_t *)a.y, a.T, a.H, a.k, a.shared);
     } else {
         const int64_t n = (int64_t)a.T * a.H;
         combine_f32<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
