@@ -163,6 +163,40 @@ def test_all_tokens_on_the_same_experts():
     assert hx.rel_err(hx.y_host(y, "bf16")[tokens], y_ref) <= hx.TOL["bf16"]
 
 
+@pytest.mark.parametrize("T,hot", [(40, True), (128, False)])
+def test_mxfp4_many_rows(T, hot):
+    """MXFP4 experts with more rows per expert than decode gives them: a bias
+    that sends all 40 tokens to the same 8 experts (row tiles of 16, 16 and 8,
+    the activation quantiser's multi-pass path), and a 128-token pass (the
+    short-pass routing with eight route workgroups)."""
+    say("[mxfp4 rows] T =", T, "hot" if hot else "")
+    c, g = layer("c4_t6")
+    c = dict(c, T=T, seed=4000 + T)
+    lay, gl = g.lay, g
+    hot_e = [3, 17, 64, 65, 130, 200, 254, 255]
+    if hot:
+        bias = np.zeros(c["E"], np.float32)
+        for r, e in enumerate(hot_e):
+            bias[e] = 100.0 - 10.0 * r  # gaps of 10, far above the logit spread
+        lay = mi.LayerData(c=c, router_w=g.lay.router_w, router_bias=bias, w_gate=g.lay.w_gate,
+                           w_up=g.lay.w_up, w_down=g.lay.w_down, s_gate=g.lay.s_gate,
+                           s_up=g.lay.s_up, s_down=g.lay.s_down)
+        gl = hx.GpuLayer(c, lay)
+    x = hx.margin_x(c, lay)
+    y, idx, w = gl.forward(hx.act_torch(x, c["act"], "cuda"))
+    idx_h = idx.cpu().numpy()
+    if hot:
+        assert (idx_h == np.array(hot_e)[None, :]).all()
+    idx_r, _, _ = oracle.route(hx.router_only_layer(c, lay), x)
+    assert np.array_equal(idx_h, idx_r)
+    tokens = np.arange(T, dtype=np.int32) if hot else np.arange(0, T, 4, dtype=np.int32)
+    experts = sorted(set(idx_r[tokens].reshape(-1).tolist()))
+    y_ref, _, _ = oracle.forward(hx.oracle_layer(c, lay, experts), x, tokens)
+    err = hx.rel_err(hx.y_host(y, c["act"])[tokens], y_ref)
+    say("[mxfp4 rows] rel err", err)
+    assert err <= hx.TOL["mxfp4"], err
+
+
 @pytest.mark.parametrize("T", [5, 100])
 def test_shared_expert_short_passes(T):
     """The shared expert (group E, every token) through the short-pass
