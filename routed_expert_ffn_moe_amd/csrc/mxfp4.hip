@@ -163,11 +163,7 @@ __device__ __forceinline__ void slice_load(MxSlice<NQ> &w, const uint8_t *cbase,
                                            const uint8_t *sbase, int q0, int s_begin, int s_end)
 {
     using W = MxSlice<NQ>;
-#pragma unroll
-    for (int s = 0; s < NQ; ++s)
-        if (s >= s_begin && s < s_end)
-            w.q[s] = *(const uint4 *)(cbase + (size_t)(q0 + s) * 1024);
-    if (s_begin == 0) {  // the scales of the whole slab go with its first part
+    if (s_begin == 0) {  // the scales of the whole slab go ahead of its codes
 #pragma unroll
         for (int i = 0; i < (NQ + 3) / 4; ++i)
             w.sc[i] = 0;
@@ -184,6 +180,10 @@ __device__ __forceinline__ void slice_load(MxSlice<NQ> &w, const uint8_t *cbase,
             w.sc[s / 4] |= v << (8 * (s % 4));
         }
     }
+#pragma unroll
+    for (int s = 0; s < NQ; ++s)
+        if (s >= s_begin && s < s_end)
+            w.q[s] = *(const uint4 *)(cbase + (size_t)(q0 + s) * 1024);
 }
 
 // One 128-wide K step (hi and lo halves) at absolute step q: the activation
@@ -220,11 +220,18 @@ __device__ __forceinline__ void mx_step(const uint4 (&b)[NB][CPW], const int (&s
         }
 }
 
+// Workgroup barrier that waits for this wave's LDS operations only (the
+// global loads in flight stay in flight).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // The tile list, its length and the group offsets come in as read-only
 // kernel arguments: uniform scalar loads, the first two issued together, so
 // a workgroup starts its weight stream one memory latency after it starts.
-template <bool GU, int CPW, int NW, int NQ>
-__global__ __launch_bounds__(64 * NW, 2) void expert_mxfp4(MxP p, const int32_t *__restrict__ ntiles,
+template <bool GU, int CPW, int NW, int NQ, bool ONE>
+__global__ __launch_bounds__(64 * NW, 3) void expert_mxfp4(MxP p, const int32_t *__restrict__ ntiles,
                                                            const Tile *__restrict__ tiles,
                                                            const int32_t *__restrict__ offsets,
                                                            const int32_t *__restrict__ row_tok)
@@ -281,38 +288,47 @@ __global__ __launch_bounds__(64 * NW, 2) void expert_mxfp4(MxP p, const int32_t 
     const int nq = nrows * nblk;  // activation blocks to stage
     const int64_t lda = GU ? p.H : p.ldh;
 
-    // Slab 0: the first half of the weights, then the first pass of
-    // activation blocks, then the second half; the activations, queued ahead
-    // of the second half, arrive while the weights still stream in.  The
-    // scheduling barriers keep that order.
-    W w[NB][CPW];
-    constexpr int H1 = NQ / 2;
-#pragma unroll
-    for (int m = 0; m < NB; ++m)
-#pragma unroll
-        for (int cb = 0; cb < CPW; ++cb)
-            slice_load<NQ>(w[m][cb], cbase[m][cb], sbase[m][cb], 0, 0, H1);
-    __builtin_amdgcn_sched_barrier(0);
+    // The tile's activation rows are quantised into LDS before any weight is
+    // requested: the registers the conversion needs are free again before
+    // the weight slice lands, so three workgroups fit on a CU and a decode
+    // grid is resident at once (no second round of workgroups).  Two blocks
+    // per thread are loaded together; only tiles of more than 8 rows loop.
     const int tid = threadIdx.x;
-    uint4 raw[4];
-    block_load(raw, block_src(p.a, src, lda, nblk, tid < nq ? tid : 0));
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int m = 0; m < NB; ++m)
-#pragma unroll
-        for (int cb = 0; cb < CPW; ++cb)
-            slice_load<NQ>(w[m][cb], cbase[m][cb], sbase[m][cb], 0, H1, NQ);
-    if (tid < nq)
-        block_quantise(raw, tid / nblk, tid % nblk, K, ahi, alo, shi, slo);
-    for (int q = tid + 64 * NW; q < nq; q += 64 * NW) {  // tiles of many rows
-        block_load(raw, block_src(p.a, src, lda, nblk, q));
-        block_quantise(raw, q / nblk, q % nblk, K, ahi, alo, shi, slo);
+    {
+        uint4 raw0[4], raw1[4];
+        const int q1 = tid + 64 * NW;
+        block_load(raw0, block_src(p.a, src, lda, nblk, tid < nq ? tid : 0));
+        block_load(raw1, block_src(p.a, src, lda, nblk, q1 < nq ? q1 : 0));
+        if (tid < nq)
+            block_quantise(raw0, tid / nblk, tid % nblk, K, ahi, alo, shi, slo);
+        if (q1 < nq)
+            block_quantise(raw1, q1 / nblk, q1 % nblk, K, ahi, alo, shi, slo);
+        for (int q = tid + 2 * 64 * NW; q < nq; q += 64 * NW) {  // tiles of many rows
+            block_load(raw0, block_src(p.a, src, lda, nblk, q));
+            block_quantise(raw0, q / nblk, q % nblk, K, ahi, alo, shi, slo);
+        }
     }
-    __syncthreads();
+    // Slab 0 of the weights, all of it in flight before the barrier, step by
+    // step across the slices (the scales of a slice go with its first step),
+    // so the MFMAs of step s wait only for the loads up to step s.
+    W w[NB][CPW];
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
+#pragma unroll
+            for (int cb = 0; cb < CPW; ++cb)
+                slice_load<NQ>(w[m][cb], cbase[m][cb], sbase[m][cb], 0, s, s + 1);
+        __builtin_amdgcn_sched_barrier(0);  // keep the issue order
+    }
+    // A barrier for the LDS stores only: __syncthreads would also wait for
+    // every weight load to land before the first MFMA.
+    lds_barrier();
     const int ar = (lane & 15) < nrows ? (lane & 15) : 0;  // rows past the tile repeat row 0
 
-    for (int q0 = 0; q0 < Q; q0 += NQ) {
-        if (q0 > 0) {
+    // ONE: K is a single slab (the slice pointers are dead once issued)
+    for (int q0 = 0; q0 < (ONE ? NQ : Q); q0 += NQ) {
+        if (!ONE && q0 > 0) {
 #pragma unroll
             for (int m = 0; m < NB; ++m)
 #pragma unroll
@@ -387,7 +403,7 @@ __global__ void pack_scales(const uint8_t *__restrict__ in, uint8_t *__restrict_
     }
 }
 
-template <bool GU, int CPW, int NW, int NQ>
+template <bool GU, int CPW, int NW, int NQ, bool ONE = false>
 void launch(const MxP &p, int N, int K, int tiles, hipStream_t st)
 {
     const size_t lds = (size_t)p.cap * (2 * (K + MX_PAD) + 2 * (K / 32));
@@ -395,21 +411,25 @@ void launch(const MxP &p, int N, int K, int tiles, hipStream_t st)
     // here is left to the launch below to report.
     static size_t granted = 48 * 1024;
     if (lds > granted &&
-        hipFuncSetAttribute((const void *)expert_mxfp4<GU, CPW, NW, NQ>,
+        hipFuncSetAttribute((const void *)expert_mxfp4<GU, CPW, NW, NQ, ONE>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess)
         granted = lds;
-    expert_mxfp4<GU, CPW, NW, NQ>
+    expert_mxfp4<GU, CPW, NW, NQ, ONE>
         <<<dim3(N / (16 * CPW * NW), tiles), 64 * NW, lds, st>>>(p, p.ntiles, p.tiles, p.offsets,
                                                                    p.row_tok);
 }
 
 // Slab width (in 128-wide K steps): the largest of 16, 8, 6, 4, 2, 1 that
-// divides K / 128.
+// divides K / 128; K of one slab of 16 or 6 steps has its own variant.
 template <bool GU, int CPW, int NW>
 void launch_k(const MxP &p, int N, int K, int tiles, hipStream_t st)
 {
     const int q = K / 128;
-    if (q % 16 == 0)
+    if (q == 16)
+        launch<GU, CPW, NW, 16, true>(p, N, K, tiles, st);
+    else if (q == 6)
+        launch<GU, CPW, NW, 6, true>(p, N, K, tiles, st);
+    else if (q % 16 == 0)
         launch<GU, CPW, NW, 16>(p, N, K, tiles, st);
     else if (q % 8 == 0)
         launch<GU, CPW, NW, 8>(p, N, K, tiles, st);
