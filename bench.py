@@ -220,6 +220,52 @@ class Workload:
         return np.bincount(idx.reshape(-1), minlength=self.c["E"])
 
 
+def ceilings():
+    """Measured ceilings of this device, beside the published peaks: the HBM
+    read rate (moe_probe_read over a 2 GiB buffer, eight times the infinity
+    cache) and the sustained bf16 MFMA rate (moe_probe_mfma, 2 waves per SIMD
+    of 8 independent 16x16x32 chains); best of 5 timed runs each."""
+    import torch
+
+    import routed_expert_ffn_moe_amd as moe
+    st = torch.cuda.current_stream()
+
+    def best_ms(f):
+        f()
+        torch.cuda.synchronize()
+        b = float("inf")
+        for _ in range(5):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            f()
+            e1.record(st)
+            e1.synchronize()
+            b = min(b, e0.elapsed_time(e1))
+        return b
+
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    t_read = best_ms(lambda: moe.moe_probe_read(buf))
+    del buf
+    waves = 8 * torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 20000
+    t_mma = best_ms(lambda: moe.moe_probe_mfma(waves, iters))
+    return {"hbm_read_GBps": round(nbytes / (t_read * 1e-3) / 1e9, 1),
+            "bf16_mfma_TFLOPs": round(waves * iters * 8 * 16384 / (t_mma * 1e-3) / 1e12, 1),
+            "probes": "moe_probe_read over 2 GiB; moe_probe_mfma, %d waves x %d rounds" % (waves, iters)}
+
+
+def with_ceiling(roof, ceil):
+    """The roofline entry plus the fraction of the measured ceiling."""
+    m = ceil["hbm_read_GBps"] if roof["bound"] == "hbm" else (
+        ceil["bf16_mfma_TFLOPs"] if roof["unit"] == "TFLOP/s" and roof["peak"] == PEAK_TFLOPS["bf16"]
+        else None)
+    if m:
+        roof = dict(roof, measured_ceiling=m, frac_of_measured=round(roof["achieved"] / m, 4))
+    return roof
+
+
 def cpu_baseline(wl, seconds):
     """The CPU oracle (as it stands) on a sample of the workload's tokens."""
     import numpy as np
@@ -281,6 +327,7 @@ def main():
     import routed_expert_ffn_moe_amd as moe
     moe.load()
     torch.cuda.set_device(0)
+    ceil = ceilings()
 
     wl = Workload(args.workload)
     wall, stages = wl.time(args.steps, args.warmup)
@@ -306,8 +353,9 @@ def main():
                    "top_k": c["top_k"], "I": c["I"], "I_shared": c["I_shared"],
                    "bias": c["bias"], "experts_touched": work["_Es"],
                    "max_rows_per_expert": int(counts.max())},
-        "roofline": dict(roofline(work, dom, stages[dom], c["w"]),
-                         traffic=measured_traffic(args.workload, dom)),
+        "roofline": with_ceiling(dict(roofline(work, dom, stages[dom], c["w"]),
+                                      traffic=measured_traffic(args.workload, dom)), ceil),
+        "ceilings": ceil,
         "stages_us": {k: round(v * 1e3, 2) for k, v in stages.items()},
         "tuning": {k: v for k, v in os.environ.items() if k.startswith("MOE_")},
     }
@@ -335,8 +383,8 @@ def main():
                       "us_per_step": round(wall2 / steps * 1e6, 2), **entry, "weight_sets": wsets,
                       "experts_touched": wk["_Es"],
                       "stages_us": {k: round(v * 1e3, 2) for k, v in st2.items()},
-                      "roofline": dict(roofline(wk, d2, st2[d2], cc["w"]),
-                                       traffic=measured_traffic(name, d2))}
+                      "roofline": with_ceiling(dict(roofline(wk, d2, st2[d2], cc["w"]),
+                                                    traffic=measured_traffic(name, d2)), ceil)}
         del w2
         torch.cuda.empty_cache()
     out["also"] = also

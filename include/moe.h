@@ -158,6 +158,21 @@ int moe_pack_bf16(int E, int N, int K, const void *w, void *w_out, void *stream)
 int moe_stage_timing_enable(int on);
 int moe_stage_timing_read(float *ms, int n_stages, int *n_calls);
 
+/* Measurement aids (not part of the layer): the ceilings its kernels are
+ * compared with on this device.  Asynchronous on `stream`; time them with
+ * events around the call.
+ * moe_probe_read reads `bytes` (a positive multiple of 16) at the device
+ * pointer buf with 16-byte loads from every CU and discards the data, so a
+ * buffer much larger than the caches gives the achievable HBM read rate.
+ * moe_probe_mfma runs `iters` rounds of 8 independent bf16 16x16x32 MFMA
+ * chains in each of `waves` waves (a positive multiple of 4): 8 * 16384
+ * floating-point operations per wave and round, the matrix cores' sustained
+ * bf16 rate.  sink is a device int (or NULL) that may receive a value
+ * derived from the results.  MOE_EINVAL for bad sizes or a NULL buffer,
+ * MOE_EHIP if the launch fails. */
+int moe_probe_read(const void *buf, size_t bytes, void *stream);
+int moe_probe_mfma(int waves, int iters, int *sink, void *stream);
+
 /* Static text for a return code. */
 const char *moe_strerror(int code);
 

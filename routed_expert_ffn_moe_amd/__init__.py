@@ -19,7 +19,7 @@ __all__ = [
     "MOE_EUNSUPPORTED", "MOE_EHIP", "MoeError", "moe_shape_t", "moe_weights_t", "make_shape",
     "make_weights", "moe_workspace_bytes", "moe_forward", "moe_route", "moe_strerror",
     "moe_last_error", "moe_stage_timing_enable", "moe_stage_timing_read", "moe_pack_bf16",
-    "pack_bf16", "moe_pack_mxfp4", "pack_mxfp4", "STAGES",
+    "pack_bf16", "moe_pack_mxfp4", "pack_mxfp4", "STAGES", "moe_probe_read", "moe_probe_mfma",
     "lib_path", "load",
 ]
 
@@ -80,6 +80,10 @@ def load() -> ctypes.CDLL:
         lib.moe_pack_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P]
         lib.moe_pack_mxfp4.restype = ctypes.c_int
         lib.moe_pack_mxfp4.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
+        lib.moe_probe_read.restype = ctypes.c_int
+        lib.moe_probe_read.argtypes = [P, ctypes.c_size_t, P]
+        lib.moe_probe_mfma.restype = ctypes.c_int
+        lib.moe_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, P, P]
         _lib = lib
     return _lib
 
@@ -194,6 +198,17 @@ def moe_stage_timing_read():
     n = ctypes.c_int(0)
     _check(load().moe_stage_timing_read(ms, len(STAGES), ctypes.byref(n)))
     return dict(zip(STAGES, [float(v) for v in ms])), n.value
+
+
+def moe_probe_read(buf, stream=None) -> None:
+    """Stream-read the device tensor `buf` (measurement aid, see moe.h)."""
+    n = buf.numel() * buf.element_size()
+    _check(load().moe_probe_read(_ptr(buf), n - n % 16, _stream(stream)))
+
+
+def moe_probe_mfma(waves: int, iters: int, stream=None) -> None:
+    """bf16 MFMA chains on every wave (measurement aid, see moe.h)."""
+    _check(load().moe_probe_mfma(waves, iters, None, _stream(stream)))
 
 
 def moe_strerror(code: int) -> str:

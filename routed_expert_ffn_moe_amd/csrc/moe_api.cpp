@@ -570,4 +570,20 @@ int moe_stage_timing_read(float *ms, int n_stages, int *n_calls)
     return rc;
 }
 
+int moe_probe_read(const void *buf, size_t bytes, void *stream)
+{
+    if (!buf || bytes == 0 || bytes % 16 != 0)
+        return fail(MOE_EINVAL, "moe_probe_read: buf and a positive multiple of 16 bytes");
+    moe::launch_probe_read(buf, bytes, nullptr, (hipStream_t)stream);
+    return launched("probe_read");
+}
+
+int moe_probe_mfma(int waves, int iters, int *sink, void *stream)
+{
+    if (waves <= 0 || waves % 4 != 0 || iters <= 0)
+        return fail(MOE_EINVAL, "moe_probe_mfma: waves a positive multiple of 4, iters > 0");
+    moe::launch_probe_mfma(waves, iters, sink, (hipStream_t)stream);
+    return launched("probe_mfma");
+}
+
 }  // extern "C"

@@ -1,0 +1,78 @@
+// Measurement aids: the ceilings the layer's kernels are compared with on
+// the device they run on (not part of the layer's computation).
+//
+//  probe_read: every CU streams 16-byte loads over a buffer (grid-stride,
+//              8 loads in flight per thread) and discards the data: the
+//              achievable HBM read rate for a buffer far larger than the
+//              caches.
+//  probe_mfma: each wave runs 8 independent chains of bf16 16x16x32 MFMAs
+//              on register operands: the matrix cores' sustained rate.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int PR_NL = 8;
+
+__global__ __launch_bounds__(256) void probe_read(const uint4 *__restrict__ src, size_t n16,
+                                                  int *__restrict__ sink)
+{
+    uint32_t x = 0;
+    const size_t stride = (size_t)gridDim.x * 256 * PR_NL;
+    for (size_t base = (size_t)blockIdx.x * 256 * PR_NL + threadIdx.x; base < n16;
+         base += stride) {
+        uint4 v[PR_NL];
+#pragma unroll
+        for (int j = 0; j < PR_NL; ++j) {
+            const size_t i = base + (size_t)j * 256;
+            v[j] = i < n16 ? src[i] : uint4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int j = 0; j < PR_NL; ++j)
+            x ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    }
+    if (x == 0x9E3779B9u && sink)  // practically never: keeps the loads
+        *sink = (int)x;
+}
+
+__global__ __launch_bounds__(256) void probe_mfma(int iters, int *__restrict__ sink)
+{
+    const uint32_t lane = threadIdx.x & 63;
+    // operands near 1 (bf16 0x3F80 = 1.0), different per lane
+    const uint32_t a0 = 0x3F803F80u + (lane & 7), b0 = 0x3F803F80u + (lane >> 3);
+    const bf16x8 a = as_bf16x8(uint4{a0, a0 + 1, a0 + 2, a0 + 3});
+    const bf16x8 b = as_bf16x8(uint4{b0, b0 + 1, b0 + 2, b0 + 3});
+    floatx4 acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        acc[j] = floatx4{0, 0, 0, 0};
+    // in place in the accumulation registers (the compiler's own form
+    // copies the accumulators out and back every round)
+    for (int i = 0; i < iters; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            mfma16_acc(acc[j], a, b);
+    mfma_acc_drain();
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+    if (blockIdx.x == 0 && threadIdx.x == 0 && sink)
+        *sink = (int)s;
+}
+
+}  // namespace
+
+void launch_probe_read(const void *buf, size_t bytes, int *sink, hipStream_t st)
+{
+    probe_read<<<512, 256, 0, st>>>((const uint4 *)buf, bytes / 16, sink);
+}
+
+void launch_probe_mfma(int waves, int iters, int *sink, hipStream_t st)
+{
+    probe_mfma<<<waves / 4, 256, 0, st>>>(iters, sink);
+}
+
+}  // namespace moe

@@ -162,3 +162,16 @@ def test_pack_bf16_rejects_bad_arguments(E, N, K, ptrs):
     rc = lib.moe_pack_bf16(E, N, K, *[ctypes.c_void_p(p) for p in ptrs], None)
     assert rc == moe.MOE_EINVAL
     assert "moe_pack_bf16" in moe.moe_last_error()
+
+
+def test_probe_argument_checks():
+    """The measurement probes reject bad sizes before launching anything."""
+    lib = moe.load()
+    buf = ctypes.c_void_p(0x7F1000000000)
+    assert lib.moe_probe_read(None, 1 << 20, None) == moe.MOE_EINVAL
+    assert lib.moe_probe_read(buf, 0, None) == moe.MOE_EINVAL
+    assert lib.moe_probe_read(buf, (1 << 20) + 8, None) == moe.MOE_EINVAL
+    assert lib.moe_probe_mfma(0, 10, None, None) == moe.MOE_EINVAL
+    assert lib.moe_probe_mfma(6, 10, None, None) == moe.MOE_EINVAL
+    assert lib.moe_probe_mfma(8, 0, None, None) == moe.MOE_EINVAL
+    assert "probe" in moe.moe_last_error()

@@ -309,3 +309,11 @@ def test_pack_bf16_layout():
                         want[e, gg, s, c, lane] = a[e, n, 32 * s + 8 * b:32 * s + 8 * b + 8]
     got = pw.view(torch.int16).cpu().numpy()
     assert np.array_equal(got.reshape(-1), want.reshape(-1))
+
+
+def test_measurement_probes_run():
+    """The ceiling probes the benchmark reports run to completion."""
+    buf = torch.ones(1 << 18, dtype=torch.int32, device="cuda")
+    moe.moe_probe_read(buf)
+    moe.moe_probe_mfma(8, 16)
+    torch.cuda.synchronize()
