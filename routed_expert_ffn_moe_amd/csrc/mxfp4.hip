@@ -36,6 +36,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <cstdlib>
 
 namespace moe {
 
@@ -470,11 +471,27 @@ void run(const ExpertArgs &a, hipStream_t st)
     if (tiles == 0)
         return;
     // N is a multiple of 128 (checked at the boundary).  Gate+up: 16 columns
-    // of both matrices per wave; down: 32 columns per wave.
-    if (GU)
-        launch_k<true, 1, 4>(p, N, K, tiles, st);
+    // of both matrices per wave; down: 32 columns per wave.  Tiles of at most
+    // 8 rows (decode and verify) take two waves per workgroup: twice the
+    // workgroups spread the weight bytes more evenly over the CUs (a CU
+    // pulls its share at its own rate; at T=6 four waves leave a fifth of
+    // the CUs a third more bytes than the rest), and the activation rows
+    // each workgroup quantises are few.  Fuller tiles take four, which
+    // quantise their rows once for 64 columns.  MOE_MX_NW (1, 2 or 4)
+    // overrides the choice for tuning runs (read once per process).
+    static const int forced = [] {
+        const char *e = getenv("MOE_MX_NW");
+        const int v = e ? atoi(e) : 0;
+        return (v == 1 || v == 2 || v == 4) ? v : 0;
+    }();
+    constexpr int CPW = GU ? 1 : 2;
+    const int nw = forced ? forced : p.cap <= 8 ? 2 : 4;
+    if (nw == 4)
+        launch_k<GU, CPW, 4>(p, N, K, tiles, st);
+    else if (nw == 2)
+        launch_k<GU, CPW, 2>(p, N, K, tiles, st);
     else
-        launch_k<false, 2, 4>(p, N, K, tiles, st);
+        launch_k<GU, CPW, 1>(p, N, K, tiles, st);
 }
 
 }  // namespace
