@@ -9,10 +9,11 @@
 // here every pair is placed exactly once by a single counting pass), and
 // "MoE prefill quantum" (cause section: tokens per expert set the cost).
 //
-// Determinism: counts use LDS atomics (order-free); positions come from
-// ballot-based ranks inside waves that walk their pairs in order, so the
-// grouped order is t ascending, then j, within every expert, the same as a
-// stable counting sort.
+// Determinism: counts use integer atomics (order-free), in LDS here or in
+// global memory where the segmented router's top-k kernel counts the block
+// histogram; positions come from ballot-based ranks inside waves that walk
+// their pairs in order, so the grouped order is t ascending, then j, within
+// every expert, the same as a stable counting sort.
 #include "common.h"
 #include "kernels.h"
 
