@@ -53,7 +53,9 @@ CONFIGS: Dict[str, dict] = {
                   bias=None, layer="L4", seed=5,
                   desc="decode row, MXFP4 experts: T=1 H=2048 E=256 top-8 I=768"),
 }
-LAYER_SEED = {"L0": 100, "L1": 101, "L3": 103, "L4": 104}
+LAYER_SEED = {"L0": 100, "L1": 101, "L3": 103, "L4": 104,
+              # small layers of other shapes (the tests' sweep of kernel variants)
+              "SA": 201, "SB": 202, "SC": 203, "SD": 204, "SE": 205, "SF": 206, "SG": 207}
 W_STD = 0.02      # std of router and expert weights
 MARGIN = 1e-3     # minimum top-k logit gap of accepted token rows
 

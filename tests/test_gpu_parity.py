@@ -217,6 +217,39 @@ def test_shared_expert_short_passes(T):
     assert err <= hx.TOL[c["w"]], err
 
 
+# Small layers whose shapes take the other kernel variants: the router
+# without the 16-expert tiles, router_gemm (E not a multiple of 128), the
+# tiled GEMMs where the streaming kernels do not apply (H % 256, I < 512, a
+# shared expert of another width), MXFP4 slabs of one 128-wide step and of 16
+# steps over a 4096-wide K, the segmented router with one expert block, fp32.
+SWEEP = {
+    "SA": dict(T=50, H=384, E=24, top_k=3, I=192, I_shared=0, act="bf16", w="bf16", bias=None),
+    "SB": dict(T=200, H=1024, E=64, top_k=4, I=256, I_shared=0, act="bf16", w="bf16",
+               bias="uniform"),
+    "SC": dict(T=40, H=512, E=16, top_k=2, I=256, I_shared=384, act="bf16", w="bf16", bias=None),
+    "SD": dict(T=10, H=640, E=32, top_k=4, I=384, I_shared=0, act="bf16", w="mxfp4", bias=None),
+    "SE": dict(T=3, H=4096, E=16, top_k=2, I=512, I_shared=0, act="bf16", w="mxfp4", bias=None),
+    "SF": dict(T=33, H=128, E=5, top_k=2, I=64, I_shared=0, act="f32", w="f32", bias=None),
+    "SG": dict(T=300, H=2048, E=128, top_k=2, I=512, I_shared=0, act="bf16", w="bf16", bias=None),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SWEEP))
+def test_shape_sweep(name):
+    say("[sweep]", name, SWEEP[name])
+    c = dict(SWEEP[name], layer=name, seed=5000 + ord(name[1]), desc=name)
+    lay = mi.make_layer(c, "cuda")
+    g = hx.GpuLayer(c, lay)
+    x = hx.margin_x(c, lay)
+    y, idx, w = g.forward(hx.act_torch(x, c["act"], "cuda"))
+    y_ref, idx_r, w_r = oracle.forward(hx.oracle_layer(c, lay), x)
+    assert np.array_equal(idx.cpu().numpy(), idx_r)
+    assert np.abs(w.cpu().numpy() - w_r).max() <= hx.W_TOL
+    err = hx.rel_err(hx.y_host(y, c["act"]), y_ref)
+    say("[sweep]", name, "rel err", err)
+    assert err <= hx.TOL[c["w"]], err
+
+
 def test_zero_tokens_is_a_no_op():
     c, g = layer("c1")
     xd = torch.empty((0, c["H"]), dtype=torch.bfloat16, device="cuda")
