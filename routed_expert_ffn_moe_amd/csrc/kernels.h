@@ -87,6 +87,9 @@ struct ExpertArgs {
     const Tile *tiles_dc;
     const int32_t *ntiles_dc;
     const int4 *items_gu, *items_dc;       // work items of the streaming kernels
+    const int32_t *topk_idx;                 // [T*k] expert of each pair
+    const int32_t *row_of;                   // [T*k] grouped row of each pair
+    void *y;                                 // [T, H] act: the layer output
     int max_tiles_gu, max_tiles_dc;
     int T, H, E, k, I, I_shared, act, wdt;
     int shape_T;  // tokens of a full pass: selects the tile shape
@@ -107,6 +110,11 @@ void launch_stream(const ExpertArgs &a, bool gu, hipStream_t st);
 int mxfp4_bm();
 void launch_gate_up_mxfp4(const ExpertArgs &a, hipStream_t st);
 void launch_down_mxfp4(const ExpertArgs &a, hipStream_t st);
+// Decode rows (T <= 8, top_k <= 8, MXFP4, no shared expert, I <= 1024): the down
+// projection of every (t, j) pair and the weighted combine in one kernel,
+// writing y directly (the staging rows and the combine pass are skipped).
+bool down_combine_mxfp4_ok(const ExpertArgs &a);
+void launch_down_combine_mxfp4(const ExpertArgs &a, hipStream_t st);
 // OCP row-major MXFP4 (codes [E, N, K/2], scales [E, N, K/32]) into the
 // packed layout the MXFP4 kernels read.
 void launch_pack_mxfp4(int E, int N, int K, const uint8_t *codes, const uint8_t *scales,

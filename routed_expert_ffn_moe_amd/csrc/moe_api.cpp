@@ -399,6 +399,9 @@ int moe_forward(const moe_shape_t *s, const moe_weights_t *w, const void *x, voi
         a.items_gu = (const int4 *)(wsb + Lw.items_gu);
         a.items_dc = (const int4 *)(wsb + Lw.items_dc);
         a.ntiles_dc = (const int32_t *)(wsb + Lw.ntiles) + 1;
+        a.topk_idx = idx;
+        a.row_of = (const int32_t *)(wsb + Lw.row_of);
+        a.y = yc;
         a.max_tiles_gu = Lw.max_tiles_gu;
         a.max_tiles_dc = Lw.max_tiles_dc;
         {
@@ -407,6 +410,15 @@ int moe_forward(const moe_shape_t *s, const moe_weights_t *w, const void *x, voi
         }
         if ((rc = launched("gate_up")))
             return rc;
+        if (moe::down_combine_mxfp4_ok(a)) {  // decode rows: y straight from the down kernel
+            {
+                StageScope sc(3, st);
+                moe::launch_down_combine_mxfp4(a, st);
+            }
+            if ((rc = launched("down")))
+                return rc;
+            continue;
+        }
         {
             StageScope sc(3, st);
             moe::launch_down(a, st);

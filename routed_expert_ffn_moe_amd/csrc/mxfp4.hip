@@ -370,6 +370,72 @@ __global__ __launch_bounds__(64 * NW, 3) void expert_mxfp4(MxP p, const int32_t 
     }
 }
 
+// Down projection and combine for decode rows, one workgroup per (16 output
+// columns, token t): wave j takes pair (t, j) - its expert's 16 weight rows
+// over the whole K, and its h row, quantised by the wave into its own LDS
+// area - and rounds its 16 outputs to bf16 as a staging row would be; then
+// y[t] over those columns is the sum over j in order of w[t, j] times them,
+// in fp32, rounded once: the same arithmetic as the down kernel followed by
+// the combine, without the staging rows or the extra launch.  A few experts
+// shared by two of the rows are streamed twice (a T=6 block has 47 experts
+// for 48 pairs).
+struct MxTokP {
+    const uint16_t *h;           // [rows, ldh]
+    const uint8_t *c, *s;        // down codes / scales, packed
+    const int32_t *idx, *row_of;
+    const float *w;
+    uint16_t *y;                 // [T, H]
+    int H, E, k, I, ldh;
+};
+
+template <int NQ>
+__global__ __launch_bounds__(512) void expert_mxfp4_down_tok(MxTokP p)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
+    const int t = blockIdx.y, cb = blockIdx.x;  // output columns 16*cb .. +15
+    const int K = p.I, nblk = K / 32, ld = K + MX_PAD;
+    const int wst = (2 * ld + 2 * nblk + 15) & ~15;  // a wave's LDS area (16-byte aligned)
+    const int pr = t * p.k + j;
+    const int e = __builtin_amdgcn_readfirstlane(p.idx[pr]);
+    const int row = __builtin_amdgcn_readfirstlane(p.row_of[pr]);
+    uint8_t *ahi = smem + j * wst;
+    uint8_t *alo = ahi + ld, *shi = alo + ld, *slo = shi + nblk;
+    float *s_o = (float *)(smem + p.k * wst);  // [k][64]
+    // this pair's h row, one 32-element block per lane (nblk <= 64)
+    if (lane < nblk) {
+        uint4 raw[4];
+        block_load(raw, p.h + (int64_t)row * p.ldh + lane * 32);
+        block_quantise(raw, 0, lane, K, ahi, alo, shi, slo);
+    }
+    // the expert's 16 weight rows of this column block, scales first
+    // (measured: issuing them ahead of the h row is no faster)
+    const int64_t blk = (int64_t)e * (p.H / 16) + cb;
+    MxSlice<NQ> w;
+    slice_load<NQ>(w, p.c + blk * NQ * 1024 + 16 * lane, p.s + (blk * 64 + lane) * NQ, 0, 0, NQ);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS rows
+    __builtin_amdgcn_wave_barrier();
+    floatx4 acc[1][1] = {{floatx4{0, 0, 0, 0}}};
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+        const uint4 b[1][1] = {{w.q[s]}};
+        const int sb[1][1] = {{(int)(w.sc[s / 4] >> (8 * (s % 4)) & 0xFF)}};
+        mx_step<1, 1>(b, sb, ahi, alo, shi, slo, ld, nblk, s, 0, acc);
+    }
+    // Row 0 of C is in lanes 0..15, element 0 (column 16*cb + lane).  Every
+    // lane stores its element: a store under a lane condition would let the
+    // compiler sink the MFMAs into that branch, where they would run with
+    // part of the wave masked off.
+    s_o[j * 64 + lane] = bf2f(f2bf(acc[0][0][0]));
+    __syncthreads();
+    if (j == 0 && lane < 16) {
+        float v = 0.0f;
+        for (int q = 0; q < p.k; ++q)
+            v = fmaf(p.w[t * p.k + q], s_o[q * 64 + lane], v);
+        p.y[(int64_t)t * p.H + 16 * cb + lane] = f2bf(v);
+    }
+}
+
 // Repacking from the OCP row-major form: one thread per 16 code bytes, and
 // one per scale byte.
 __global__ void pack_codes(const uint8_t *__restrict__ in, uint8_t *__restrict__ out, int E, int N,
@@ -503,6 +569,47 @@ void launch_pack_mxfp4(int E, int N, int K, const uint8_t *codes, const uint8_t 
     const unsigned grid = (unsigned)std::min<int64_t>((chunks + 255) / 256, 65536);
     pack_codes<<<grid, 256, 0, st>>>(codes, codes_out, E, N, K);
     pack_scales<<<grid, 256, 0, st>>>(scales, scales_out, E, N, K);
+}
+
+bool down_combine_mxfp4_ok(const ExpertArgs &a)
+{
+    return a.wdt == W_MXFP4 && a.act == ACT_BF16 && a.T >= 1 && a.T <= 8 && a.I_shared == 0 &&
+           a.k <= 8 && a.I % 128 == 0 && a.I <= 1024 && a.topk_idx && a.row_of && a.y;
+}
+
+template <int NQ>
+static void down_tok(const MxTokP &p, int T, hipStream_t st)
+{
+    const size_t wst = (2 * (p.I + MX_PAD) + 2 * (p.I / 32) + 15) & ~(size_t)15;
+    const size_t lds = (size_t)p.k * wst + (size_t)p.k * 64 * 4;
+    expert_mxfp4_down_tok<NQ><<<dim3(p.H / 16, T), 64 * p.k, lds, st>>>(p);
+}
+
+void launch_down_combine_mxfp4(const ExpertArgs &a, hipStream_t st)
+{
+    MxTokP p;
+    p.h = (const uint16_t *)a.h;
+    p.c = (const uint8_t *)a.w_down;
+    p.s = a.s_down;
+    p.idx = a.topk_idx;
+    p.row_of = a.row_of;
+    p.w = a.topk_w;
+    p.y = (uint16_t *)a.y;
+    p.H = a.H;
+    p.E = a.E;
+    p.k = a.k;
+    p.I = a.I;
+    p.ldh = a.I;
+    switch (a.I / 128) {  // the whole K in one slab (I <= 1024)
+    case 1: down_tok<1>(p, a.T, st); break;
+    case 2: down_tok<2>(p, a.T, st); break;
+    case 3: down_tok<3>(p, a.T, st); break;
+    case 4: down_tok<4>(p, a.T, st); break;
+    case 5: down_tok<5>(p, a.T, st); break;
+    case 6: down_tok<6>(p, a.T, st); break;
+    case 7: down_tok<7>(p, a.T, st); break;
+    default: down_tok<8>(p, a.T, st); break;
+    }
 }
 
 void launch_gate_up_mxfp4(const ExpertArgs &a, hipStream_t st) { run<true>(a, st); }
