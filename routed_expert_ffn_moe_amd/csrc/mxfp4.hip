@@ -370,10 +370,10 @@ __global__ __launch_bounds__(64 * NW, 3) void expert_mxfp4(MxP p, const int32_t 
     }
 }
 
-// Down projection and combine for decode rows, one workgroup per (16 output
-// columns, token t): wave j takes pair (t, j) - its expert's 16 weight rows
-// over the whole K, and its h row, quantised by the wave into its own LDS
-// area - and rounds its 16 outputs to bf16 as a staging row would be; then
+// Down projection and combine for decode rows, one workgroup per (16 CB
+// output columns, token t): wave j takes pair (t, j) - its expert's 16 CB
+// weight rows over the whole K, and its h row, quantised by the wave into its
+// own LDS area - and rounds its outputs to bf16 as a staging row would be; then
 // y[t] over those columns is the sum over j in order of w[t, j] times them,
 // in fp32, rounded once: the same arithmetic as the down kernel followed by
 // the combine, without the staging rows or the extra launch.  A few experts
@@ -388,12 +388,12 @@ struct MxTokP {
     int H, E, k, I, ldh;
 };
 
-template <int NQ>
+template <int NQ, int CB>
 __global__ __launch_bounds__(512) void expert_mxfp4_down_tok(MxTokP p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
-    const int t = blockIdx.y, cb = blockIdx.x;  // output columns 16*cb .. +15
+    const int t = blockIdx.y, cb0 = blockIdx.x * CB;  // output columns 16*cb0 .. 16*(cb0+CB)-1
     const int K = p.I, nblk = K / 32, ld = K + MX_PAD;
     const int wst = (2 * ld + 2 * nblk + 15) & ~15;  // a wave's LDS area (16-byte aligned)
     const int pr = t * p.k + j;
@@ -401,38 +401,53 @@ __global__ __launch_bounds__(512) void expert_mxfp4_down_tok(MxTokP p)
     const int row = __builtin_amdgcn_readfirstlane(p.row_of[pr]);
     uint8_t *ahi = smem + j * wst;
     uint8_t *alo = ahi + ld, *shi = alo + ld, *slo = shi + nblk;
-    float *s_o = (float *)(smem + p.k * wst);  // [k][64]
+    float *s_o = (float *)(smem + p.k * wst);  // [k][CB][64]
     // this pair's h row, one 32-element block per lane (nblk <= 64)
     if (lane < nblk) {
         uint4 raw[4];
         block_load(raw, p.h + (int64_t)row * p.ldh + lane * 32);
         block_quantise(raw, 0, lane, K, ahi, alo, shi, slo);
     }
-    // the expert's 16 weight rows of this column block, scales first
+    // the expert's 16-row weight blocks of these columns, scales first
     // (measured: issuing them ahead of the h row is no faster)
-    const int64_t blk = (int64_t)e * (p.H / 16) + cb;
-    MxSlice<NQ> w;
-    slice_load<NQ>(w, p.c + blk * NQ * 1024 + 16 * lane, p.s + (blk * 64 + lane) * NQ, 0, 0, NQ);
+    MxSlice<NQ> w[CB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+        const int64_t blk = (int64_t)e * (p.H / 16) + cb0 + c;
+        slice_load<NQ>(w[c], p.c + blk * NQ * 1024 + 16 * lane, p.s + (blk * 64 + lane) * NQ, 0, 0,
+                       NQ);
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS rows
     __builtin_amdgcn_wave_barrier();
-    floatx4 acc[1][1] = {{floatx4{0, 0, 0, 0}}};
+    floatx4 acc[1][CB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+        acc[0][c] = floatx4{0, 0, 0, 0};
 #pragma unroll
     for (int s = 0; s < NQ; ++s) {
-        const uint4 b[1][1] = {{w.q[s]}};
-        const int sb[1][1] = {{(int)(w.sc[s / 4] >> (8 * (s % 4)) & 0xFF)}};
-        mx_step<1, 1>(b, sb, ahi, alo, shi, slo, ld, nblk, s, 0, acc);
+        uint4 b[1][CB];
+        int sb[1][CB];
+#pragma unroll
+        for (int c = 0; c < CB; ++c) {
+            b[0][c] = w[c].q[s];
+            sb[0][c] = (int)(w[c].sc[s / 4] >> (8 * (s % 4)) & 0xFF);
+        }
+        mx_step<1, CB>(b, sb, ahi, alo, shi, slo, ld, nblk, s, 0, acc);
     }
     // Row 0 of C is in lanes 0..15, element 0 (column 16*cb + lane).  Every
-    // lane stores its element: a store under a lane condition would let the
+    // lane stores its elements: a store under a lane condition would let the
     // compiler sink the MFMAs into that branch, where they would run with
     // part of the wave masked off.
-    s_o[j * 64 + lane] = bf2f(f2bf(acc[0][0][0]));
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+        s_o[(j * CB + c) * 64 + lane] = bf2f(f2bf(acc[0][c][0]));
     __syncthreads();
-    if (j == 0 && lane < 16) {
+    if (j == 0 && lane < 16 * CB) {
+        const int c = lane >> 4, n = lane & 15;
         float v = 0.0f;
         for (int q = 0; q < p.k; ++q)
-            v = fmaf(p.w[t * p.k + q], s_o[q * 64 + lane], v);
-        p.y[(int64_t)t * p.H + 16 * cb + lane] = f2bf(v);
+            v = fmaf(p.w[t * p.k + q], s_o[(q * CB + c) * 64 + n], v);
+        p.y[(int64_t)t * p.H + 16 * (cb0 + c) + n] = f2bf(v);
     }
 }
 
@@ -577,12 +592,23 @@ bool down_combine_mxfp4_ok(const ExpertArgs &a)
            a.k <= 8 && a.I % 128 == 0 && a.I <= 1024 && a.topk_idx && a.row_of && a.y;
 }
 
+constexpr int MX_DECODE_CUS = 256;  // compute units of an MI355X
+
 template <int NQ>
 static void down_tok(const MxTokP &p, int T, hipStream_t st)
 {
     const size_t wst = (2 * (p.I + MX_PAD) + 2 * (p.I / 32) + 15) & ~(size_t)15;
-    const size_t lds = (size_t)p.k * wst + (size_t)p.k * 64 * 4;
-    expert_mxfp4_down_tok<NQ><<<dim3(p.H / 16, T), 64 * p.k, lds, st>>>(p);
+    // Each workgroup costs its CU a fixed time (mostly its waves' h rows and
+    // their latency), so once one 16-column block per wave would need more
+    // workgroups than the device has CUs, a wave takes two blocks (measured
+    // at H=2048, top-8: T=3 to 8 pass 14.4-22.6 -> 11.5-16.2 us; T <= 2
+    // keep one block, which is slightly faster there).
+    const int cb = (p.H / 16) * T > MX_DECODE_CUS && p.H % 32 == 0 ? 2 : 1;
+    const size_t lds = (size_t)p.k * wst + (size_t)p.k * 64 * 4 * cb;
+    if (cb == 2)
+        expert_mxfp4_down_tok<NQ, 2><<<dim3(p.H / 32, T), 64 * p.k, lds, st>>>(p);
+    else
+        expert_mxfp4_down_tok<NQ, 1><<<dim3(p.H / 16, T), 64 * p.k, lds, st>>>(p);
 }
 
 void launch_down_combine_mxfp4(const ExpertArgs &a, hipStream_t st)

@@ -197,6 +197,27 @@ def test_mxfp4_many_rows(T, hot):
     assert err <= hx.TOL["mxfp4"], err
 
 
+@pytest.mark.parametrize("T", [2, 3, 8])
+def test_mxfp4_decode_sizes(T):
+    """The fused down+combine kernel of decode rows in both of its shapes:
+    one 16-column block per wave (T=2: 256 workgroups) and two (T=3 and the
+    largest fused size T=8), against the oracle on every token."""
+    say("[mxfp4 decode] T =", T)
+    c, g = layer("c4_t6")
+    c = dict(c, T=T, seed=5000 + T)
+    gl = hx.GpuLayer(c, g.lay)
+    x = hx.margin_x(c, g.lay)
+    y, idx, w = gl.forward(hx.act_torch(x, c["act"], "cuda"))
+    idx_r, w_r, _ = oracle.route(hx.router_only_layer(c, g.lay), x)
+    assert np.array_equal(idx.cpu().numpy(), idx_r)
+    tokens = np.arange(T, dtype=np.int32)
+    experts = sorted(set(idx_r.reshape(-1).tolist()))
+    y_ref, _, _ = oracle.forward(hx.oracle_layer(c, g.lay, experts), x, tokens)
+    err = hx.rel_err(hx.y_host(y, c["act"]), y_ref)
+    say("[mxfp4 decode] rel err", err)
+    assert err <= hx.TOL["mxfp4"], err
+
+
 @pytest.mark.parametrize("T", [5, 100])
 def test_shared_expert_short_passes(T):
     """The shared expert (group E, every token) through the short-pass
