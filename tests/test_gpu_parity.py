@@ -117,15 +117,22 @@ def test_chunk_invariance(name, chunk):
     assert torch.equal(y0, y1)
 
 
-def test_determinism_and_poisoned_workspace():
-    say("[determinism] c2")
-    c, g = layer("c2")
+@pytest.mark.parametrize("name", ["c2", "c4_t6", "c4_t1"])
+def test_determinism_and_poisoned_workspace(name):
+    """Bit-identical results on a workspace filled with 0xFF (the decode rows'
+    one-launch routing keeps its arrival counter there) and on the same
+    workspace again (a second call finds the first call's counter)."""
+    say("[determinism]", name)
+    c, g = layer(name)
     x = hx.margin_x(c, g.lay)
     xd = hx.act_torch(x, c["act"], "cuda")
     y0, i0, w0 = g.forward(xd)
-    y1, i1, w1 = g.forward(xd, poison=True)
-    assert torch.isfinite(y1.float()).all()
-    assert torch.equal(i0, i1) and torch.equal(w0, w1) and torch.equal(y0, y1)
+    nbytes = moe.moe_workspace_bytes(g.shape(x.shape[0], 0))
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        y1, i1, w1 = g.forward(xd, poison=rep == 0, ws=ws)
+        assert torch.isfinite(y1.float()).all()
+        assert torch.equal(i0, i1) and torch.equal(w0, w1) and torch.equal(y0, y1), rep
 
 
 @pytest.mark.parametrize("T", [1, 7, 77])
