@@ -102,11 +102,14 @@ def test_route_and_permutation_bit_exact(name, T):
     assert np.array_equal(row_src.cpu().numpy(), rr)
 
 
-@pytest.mark.parametrize("name,chunk", [("c1", 32), ("c1", 100), ("c2", 128)])
+@pytest.mark.parametrize("name,chunk", [("c1", 32), ("c1", 100), ("c2", 128), ("c3", 2048)])
 def test_chunk_invariance(name, chunk):
     """Passes of up to 128 tokens take the short-pass router and permutation,
     longer ones the long-pass kernels; both give the same logits, so the
-    layer's output does not depend on the chunk size."""
+    layer's output does not depend on the chunk size.  On the wide layer the
+    8192-token pass and its 2048-token chunks take different router tiles
+    (128 and 64 tokens) and GEMM row tiles (128 and 32 rows), shared expert
+    included: still bit-identical."""
     say("[chunk]", name, chunk)
     c, g = layer(name)
     x = hx.margin_x(c, g.lay)
