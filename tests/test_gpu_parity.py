@@ -47,7 +47,7 @@ def layer(name):
 
 
 # tokens compared row by row against the oracle (None = all)
-SAMPLE = {"c0": None, "c1": None, "c2": 192, "c3": 12, "c4_t6": None, "c4_t1": None}
+SAMPLE = {"c0": None, "c1": None, "c2": 192, "c3": 48, "c4_t6": None, "c4_t1": None}
 
 
 @pytest.mark.parametrize("name", ["c0", "c1", "c4_t6", "c4_t1", "c2", "c3"])
