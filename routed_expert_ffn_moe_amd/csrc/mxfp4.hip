@@ -402,14 +402,19 @@ __global__ __launch_bounds__(512) void expert_mxfp4_down_tok(MxTokP p)
     uint8_t *ahi = smem + j * wst;
     uint8_t *alo = ahi + ld, *shi = alo + ld, *slo = shi + nblk;
     float *s_o = (float *)(smem + p.k * wst);  // [k][CB][64]
-    // this pair's h row, one 32-element block per lane (nblk <= 64)
-    if (lane < nblk) {
-        uint4 raw[4];
+    // This pair's h row, one 32-element block per lane (nblk <= 64), and
+    // the expert's 16-row weight blocks of these columns (scales first).
+    // With one block per wave the weights are requested between the h row's
+    // load and its quantisation, so they are in flight meanwhile (a wave's
+    // loads complete in order for its wait counter: weights requested ahead
+    // of the h row would make the quantiser wait for them too); with two,
+    // holding them through the quantisation measured slower, and they
+    // follow it (T=1, 2: down 10.5 -> 10.1 us; T=6, 8: 15.5 -> 16.0 us).
+    uint4 raw[4];
+    if (lane < nblk)
         block_load(raw, p.h + (int64_t)row * p.ldh + lane * 32);
+    if (CB > 1 && lane < nblk)
         block_quantise(raw, 0, lane, K, ahi, alo, shi, slo);
-    }
-    // the expert's 16-row weight blocks of these columns, scales first
-    // (measured: issuing them ahead of the h row is no faster)
     MxSlice<NQ> w[CB];
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
@@ -417,6 +422,8 @@ __global__ __launch_bounds__(512) void expert_mxfp4_down_tok(MxTokP p)
         slice_load<NQ>(w[c], p.c + blk * NQ * 1024 + 16 * lane, p.s + (blk * 64 + lane) * NQ, 0, 0,
                        NQ);
     }
+    if (CB == 1 && lane < nblk)
+        block_quantise(raw, 0, lane, K, ahi, alo, shi, slo);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS rows
     __builtin_amdgcn_wave_barrier();
     floatx4 acc[1][CB];
