@@ -231,8 +231,8 @@ __device__ __forceinline__ void lds_barrier()
 // The tile list, its length and the group offsets come in as read-only
 // kernel arguments: uniform scalar loads, the first two issued together, so
 // a workgroup starts its weight stream one memory latency after it starts.
-template <bool GU, int CPW, int NW, int NQ, bool ONE>
-__global__ __launch_bounds__(64 * NW, 3) void expert_mxfp4(MxP p, const int32_t *__restrict__ ntiles,
+template <bool GU, int CPW, int NW, int NQ, bool ONE, bool WF = false>
+__global__ __launch_bounds__(64 * NW, WF ? 2 : 3) void expert_mxfp4(MxP p, const int32_t *__restrict__ ntiles,
                                                            const Tile *__restrict__ tiles,
                                                            const int32_t *__restrict__ offsets,
                                                            const int32_t *__restrict__ row_tok)
@@ -295,32 +295,54 @@ __global__ __launch_bounds__(64 * NW, 3) void expert_mxfp4(MxP p, const int32_t 
     // grid is resident at once (no second round of workgroups).  Two blocks
     // per thread are loaded together; only tiles of more than 8 rows loop.
     const int tid = threadIdx.x;
-    {
-        uint4 raw0[4], raw1[4];
-        const int q1 = tid + 64 * NW;
+    W w[NB][CPW];
+    auto issue_weights = [&]() {
+#pragma unroll
+        for (int s = 0; s < NQ; ++s) {
+#pragma unroll
+            for (int m = 0; m < NB; ++m)
+#pragma unroll
+                for (int cb = 0; cb < CPW; ++cb)
+                    slice_load<NQ>(w[m][cb], cbase[m][cb], sbase[m][cb], 0, s, s + 1);
+            __builtin_amdgcn_sched_barrier(0);  // keep the issue order
+        }
+    };
+    if (WF) {
+        // Grids far smaller than the chip (one decode row): the
+        // weight slab is requested right behind the first activation blocks
+        // and the quantisation waits for those blocks only (a wave's loads
+        // complete in order for its wait counter), so the two memory
+        // latencies overlap; it holds the slab's registers through the
+        // quantisation, hence two workgroups per CU.
+        uint4 raw0[4];
         block_load(raw0, block_src(p.a, src, lda, nblk, tid < nq ? tid : 0));
-        block_load(raw1, block_src(p.a, src, lda, nblk, q1 < nq ? q1 : 0));
+        __builtin_amdgcn_sched_barrier(0);
+        issue_weights();
         if (tid < nq)
             block_quantise(raw0, tid / nblk, tid % nblk, K, ahi, alo, shi, slo);
-        if (q1 < nq)
-            block_quantise(raw1, q1 / nblk, q1 % nblk, K, ahi, alo, shi, slo);
-        for (int q = tid + 2 * 64 * NW; q < nq; q += 64 * NW) {  // tiles of many rows
+        for (int q = tid + 64 * NW; q < nq; q += 64 * NW) {
             block_load(raw0, block_src(p.a, src, lda, nblk, q));
             block_quantise(raw0, q / nblk, q % nblk, K, ahi, alo, shi, slo);
         }
-    }
-    // Slab 0 of the weights, all of it in flight before the barrier, step by
-    // step across the slices (the scales of a slice go with its first step),
-    // so the MFMAs of step s wait only for the loads up to step s.
-    W w[NB][CPW];
-#pragma unroll
-    for (int s = 0; s < NQ; ++s) {
-#pragma unroll
-        for (int m = 0; m < NB; ++m)
-#pragma unroll
-            for (int cb = 0; cb < CPW; ++cb)
-                slice_load<NQ>(w[m][cb], cbase[m][cb], sbase[m][cb], 0, s, s + 1);
-        __builtin_amdgcn_sched_barrier(0);  // keep the issue order
+    } else {
+        {
+            uint4 raw0[4], raw1[4];
+            const int q1 = tid + 64 * NW;
+            block_load(raw0, block_src(p.a, src, lda, nblk, tid < nq ? tid : 0));
+            block_load(raw1, block_src(p.a, src, lda, nblk, q1 < nq ? q1 : 0));
+            if (tid < nq)
+                block_quantise(raw0, tid / nblk, tid % nblk, K, ahi, alo, shi, slo);
+            if (q1 < nq)
+                block_quantise(raw1, q1 / nblk, q1 % nblk, K, ahi, alo, shi, slo);
+            for (int q = tid + 2 * 64 * NW; q < nq; q += 64 * NW) {  // tiles of many rows
+                block_load(raw0, block_src(p.a, src, lda, nblk, q));
+                block_quantise(raw0, q / nblk, q % nblk, K, ahi, alo, shi, slo);
+            }
+        }
+        // Slab 0 of the weights, all of it in flight before the barrier, step
+        // by step across the slices (the scales of a slice go with its first
+        // step), so the MFMAs of step s wait only for the loads up to step s.
+        issue_weights();
     }
     // A barrier for the LDS stores only: __syncthreads would also wait for
     // every weight load to land before the first MFMA.
@@ -492,7 +514,7 @@ __global__ void pack_scales(const uint8_t *__restrict__ in, uint8_t *__restrict_
     }
 }
 
-template <bool GU, int CPW, int NW, int NQ, bool ONE = false>
+template <bool GU, int CPW, int NW, int NQ, bool ONE = false, bool WF = false>
 void launch(const MxP &p, int N, int K, int tiles, hipStream_t st)
 {
     const size_t lds = (size_t)p.cap * (2 * (K + MX_PAD) + 2 * (K / 32));
@@ -500,10 +522,10 @@ void launch(const MxP &p, int N, int K, int tiles, hipStream_t st)
     // here is left to the launch below to report.
     static size_t granted = 48 * 1024;
     if (lds > granted &&
-        hipFuncSetAttribute((const void *)expert_mxfp4<GU, CPW, NW, NQ, ONE>,
+        hipFuncSetAttribute((const void *)expert_mxfp4<GU, CPW, NW, NQ, ONE, WF>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess)
         granted = lds;
-    expert_mxfp4<GU, CPW, NW, NQ, ONE>
+    expert_mxfp4<GU, CPW, NW, NQ, ONE, WF>
         <<<dim3(N / (16 * CPW * NW), tiles), 64 * NW, lds, st>>>(p, p.ntiles, p.tiles, p.offsets,
                                                                    p.row_tok);
 }
@@ -511,10 +533,12 @@ void launch(const MxP &p, int N, int K, int tiles, hipStream_t st)
 // Slab width (in 128-wide K steps): the largest of 16, 8, 6, 4, 2, 1 that
 // divides K / 128; K of one slab of 16 or 6 steps has its own variant.
 template <bool GU, int CPW, int NW>
-void launch_k(const MxP &p, int N, int K, int tiles, hipStream_t st)
+void launch_k(const MxP &p, int N, int K, int tiles, hipStream_t st, bool wf = false)
 {
     const int q = K / 128;
-    if (q == 16)
+    if (NW == 2 && wf && q == 16)
+        launch<GU, CPW, NW, 16, true, true>(p, N, K, tiles, st);
+    else if (q == 16)
         launch<GU, CPW, NW, 16, true>(p, N, K, tiles, st);
     else if (q == 6)
         launch<GU, CPW, NW, 6, true>(p, N, K, tiles, st);
@@ -574,10 +598,14 @@ void run(const ExpertArgs &a, hipStream_t st)
     }();
     constexpr int CPW = GU ? 1 : 2;
     const int nw = forced ? forced : p.cap <= 8 ? 2 : 4;
+    // a single decode row: gate+up requests its weights right behind the
+    // activation row (T=1: 11.7 -> 11.3 us; at T=2 the two-per-CU bound
+    // costs more than the overlap saves, 13.9 -> 15.5 us)
+    const bool wf = GU && p.cap <= 1;
     if (nw == 4)
         launch_k<GU, CPW, 4>(p, N, K, tiles, st);
     else if (nw == 2)
-        launch_k<GU, CPW, 2>(p, N, K, tiles, st);
+        launch_k<GU, CPW, 2>(p, N, K, tiles, st, wf);
     else
         launch_k<GU, CPW, 1>(p, N, K, tiles, st);
 }
