@@ -1,0 +1,73 @@
+"""Host logic of bench.py (no GPU): the algorithmic bytes and flops of a
+stage, the roofline verdict, the reading of committed counter records, and
+the one-GPU refusal."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import moe_inputs as mi  # noqa: E402
+
+
+def _counts(E, touched):
+    c = np.zeros(E, np.int64)
+    c[:touched] = 1
+    return c
+
+
+def test_gate_up_bytes_of_the_prefill_layer():
+    """T=2048, H=2048, I=768, top-8 bf16 with 102 experts touched: the
+    weights of 102 experts (2 x 768 x 2048 bf16 each, 641,728,512 bytes), x
+    once (8,388,608) and h once (16,384 rows x 768 bf16, 25,165,824)."""
+    w = bench.stage_work(mi.cfg("c2"), _counts(256, 102))
+    assert w["_Es"] == 102
+    assert w["gate_up"][0] == 641_728_512 + 8_388_608 + 25_165_824
+    assert w["gate_up"][1] == 4.0 * 2048 * 8 * 2048 * 768  # 2 GEMMs x 2 flops per MAC
+    # down: 102 experts' 2048 x 768 weights, h read, 16,384 staging rows written
+    assert w["down"][0] == 102 * 2048 * 768 * 2 + 16_384 * 768 * 2 + 16_384 * 2048 * 2
+
+
+def test_mxfp4_weight_bytes_include_the_scales():
+    """MXFP4: 16 code bytes and one scale byte per 32 weights (17/32 byte);
+    the decode row touches 8 experts: 13,369,344 weight bytes."""
+    w = bench.stage_work(mi.cfg("c4_t1"), _counts(256, 8))
+    assert w["gate_up"][0] == 13_369_344 + 2048 * 2 + 8 * 768 * 2
+
+
+def test_roofline_picks_the_binding_resource():
+    c = mi.cfg("c2")
+    w = bench.stage_work(c, _counts(256, 102))
+    r = bench.roofline(w, "gate_up", 0.17872, "bf16")  # 178.72 us
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert r["achieved"] == pytest.approx(675_282_944 / 178.72e-6 / 1e9, rel=1e-4)
+    assert r["frac"] == pytest.approx(r["achieved"] / 8000.0, abs=1e-4)
+    # a stage whose matrix time exceeds its memory time is reported on MFMA
+    m = bench.roofline({"x": (1.0e6, 1.0e13)}, "x", 10.0, "bf16")
+    assert m["bound"] == "mfma" and m["unit"] == "TFLOP/s"
+    assert m["achieved"] == pytest.approx(1000.0) and m["frac"] == pytest.approx(0.4)
+
+
+def test_traffic_records_only_for_the_current_sources(tmp_path, monkeypatch):
+    sha = bench.kernel_sources_sha1()
+    (tmp_path / "hbm_traffic_counters.md").write_text(
+        "# summary\n"
+        '<!-- traffic {"workload": "c2", "stage": "gate_up", "bytes": 123, "sources_sha1": "%s"} -->\n'
+        '<!-- traffic {"workload": "c2", "stage": "down", "bytes": 456, "sources_sha1": "0000"} -->\n'
+        % sha)
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.measured_traffic("c2", "gate_up") == 123
+    assert bench.measured_traffic("c2", "down") is None  # taken on other kernel sources
+    assert bench.measured_traffic("c1", "gate_up") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in (r.stdout + r.stderr)
