@@ -34,7 +34,11 @@
  *     gate and up, [H, I] for down).
  *   sh_gate, sh_up [I_shared, H], sh_down [H, I_shared]   act_dtype
  *     BF16 expert matrices (routed and shared) are passed as moe_pack_bf16
- *     lays them out (below); F32 ones row-major as listed.
+ *     lays them out (below); F32 ones row-major as listed.  The caller
+ *     states which in moe_weights_t.layout: MOE_LAYOUT_PACKED is required for
+ *     BF16 and MXFP4 expert matrices, MOE_LAYOUT_ROWMAJOR for F32 ones; any
+ *     other combination is refused with MOE_EINVAL (a zero-initialised
+ *     struct says ROWMAJOR, so row-major bf16 weights never reach a kernel).
  *   topk_idx [T, top_k] int32, topk_w [T, top_k] float
  *
  * Packed MXFP4 (what the kernels read: each wave's weights are whole
@@ -55,7 +59,10 @@
  *
  * Supported combinations: act F32 with w F32; act BF16 with w BF16 or MXFP4.
  * MXFP4 needs H and I multiples of 128, at most 4096, and no shared expert
- * (MOE_EINVAL / MOE_EUNSUPPORTED otherwise).
+ * (MOE_EINVAL / MOE_EUNSUPPORTED otherwise).  One pass (chunk) of Tc tokens
+ * must keep Tc * H, Tc * E * 8 and rows * max(H, I, I_shared) below 2^31,
+ * rows = Tc * top_k (+ Tc with a shared expert); larger passes are refused
+ * with MOE_EINVAL (split them with chunk_T).
  * Every pointer except router_bias, topk_w and the unused ones is a device
  * pointer, 16-byte aligned.  The caller owns all memory; the library
  * allocates nothing per call and keeps no state between calls other than
@@ -80,6 +87,9 @@ extern "C" {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype_t;
 
+/* Layout of the expert matrices in moe_weights_t (see Layouts above). */
+enum { MOE_LAYOUT_ROWMAJOR = 0, MOE_LAYOUT_PACKED = 1 };
+
 enum {
     MOE_OK = 0,
     MOE_EINVAL = -1,       /* null/misaligned pointer, bad size or dtype  */
@@ -88,6 +98,17 @@ enum {
     MOE_EHIP = -4          /* HIP launch/runtime error                    */
 };
 
+/* Sizes of one call.
+ *  - top_k is a run-time value, not a property of the weights: a caller may
+ *    run a layer with fewer experts per token than it was trained with ("Jetson
+ *    Orin Nano MoE: GPU clock floor and expert cache", section on decode time
+ *    as a fixed part plus a read part, where the model's experts-per-token
+ *    count is overridden from 8 to 4).
+ *  - chunk_T is the prefill quantum: the number of tokens the layer is handed
+ *    at a time ("MoE prefill quantum", the one-line summary and the inverse
+ *    equation quantum = target tokens per expert x E / top_k).  Passes of
+ *    chunk_T tokens run one after the other on one workspace; tokens are
+ *    independent, so y does not depend on it. */
 typedef struct {
     int32_t T;         /* tokens                                             */
     int32_t H;         /* hidden size (multiple of 64)                       */
@@ -106,6 +127,7 @@ typedef struct {
     const void *w_gate, *w_up, *w_down;      /* codes when w_dtype == MXFP4  */
     const uint8_t *s_gate, *s_up, *s_down;   /* E8M0, MXFP4 only             */
     const void *sh_gate, *sh_up, *sh_down;   /* I_shared > 0 only            */
+    int32_t layout;  /* MOE_LAYOUT_* of the expert and shared matrices       */
 } moe_weights_t;
 
 /* Bytes of device workspace moe_forward / moe_route need for `shape`
@@ -114,7 +136,10 @@ typedef struct {
 size_t moe_workspace_bytes(const moe_shape_t *shape);
 
 /* The whole layer: y [T, H] and the routing (topk_idx required, topk_w
- * nullable).  `ws` is device memory of at least moe_workspace_bytes(shape)
+ * nullable).  The routing is returned because callers keep it: per-layer
+ * logs of the experts the router chose are what an expert cache's policy is
+ * chosen from ("Jetson Orin Nano MoE: GPU clock floor and expert cache",
+ * section on choosing what to cache from the router's records).  `ws` is device memory of at least moe_workspace_bytes(shape)
  * bytes, 256-byte aligned, owned by the caller; its contents on entry do not
  * matter.  The result does not depend on chunk_T beyond rounding order: each
  * chunk is processed independently in token order. */

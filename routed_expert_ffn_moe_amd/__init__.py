@@ -15,8 +15,8 @@ import os
 from typing import Optional
 
 __all__ = [
-    "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_OK", "MOE_EINVAL", "MOE_EWORKSPACE",
-    "MOE_EUNSUPPORTED", "MOE_EHIP", "MoeError", "moe_shape_t", "moe_weights_t", "make_shape",
+    "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_LAYOUT_ROWMAJOR", "MOE_LAYOUT_PACKED", "MOE_OK",
+    "MOE_EINVAL", "MOE_EWORKSPACE", "MOE_EUNSUPPORTED", "MOE_EHIP", "MoeError", "moe_shape_t", "moe_weights_t", "make_shape",
     "make_weights", "moe_workspace_bytes", "moe_forward", "moe_route", "moe_strerror",
     "moe_last_error", "moe_stage_timing_enable", "moe_stage_timing_read", "moe_pack_bf16",
     "pack_bf16", "moe_pack_mxfp4", "pack_mxfp4", "STAGES", "moe_probe_read", "moe_probe_mfma",
@@ -24,6 +24,7 @@ __all__ = [
 ]
 
 MOE_F32, MOE_BF16, MOE_MXFP4 = 0, 1, 2
+MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_PACKED = 0, 1
 MOE_OK, MOE_EINVAL, MOE_EWORKSPACE, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3, -4
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp4": MOE_MXFP4}
 
@@ -48,7 +49,7 @@ class moe_shape_t(ctypes.Structure):
 class moe_weights_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("router_w", "router_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up",
-                 "s_down", "sh_gate", "sh_up", "sh_down")]
+                 "s_down", "sh_gate", "sh_up", "sh_down")] + [("layout", ctypes.c_int32)]
 
 
 _lib = None
@@ -115,14 +116,24 @@ def make_shape(T, H, E, top_k, I, I_shared=0, chunk_T=0, act="bf16", w="bf16") -
 class _Weights:
     """moe_weights_t plus references keeping the tensors alive."""
 
-    def __init__(self, **tensors):
+    def __init__(self, layout, **tensors):
         self._keep = tensors
-        self.c = moe_weights_t(**{k: _ptr(v) for k, v in tensors.items()})
+        self.c = moe_weights_t(**{k: _ptr(v) for k, v in tensors.items()}, layout=layout)
+
+
+def _is_packed(t) -> bool:
+    return t is not None and getattr(t, "_moe_layout", None) == "packed"
 
 
 def make_weights(router_w, w_gate, w_up, w_down, router_bias=None, s_gate=None, s_up=None,
-                 s_down=None, sh_gate=None, sh_up=None, sh_down=None) -> _Weights:
-    return _Weights(router_w=router_w, router_bias=router_bias, w_gate=w_gate, w_up=w_up,
+                 s_down=None, sh_gate=None, sh_up=None, sh_down=None, layout=None) -> _Weights:
+    """The weight struct.  `layout` (MOE_LAYOUT_*) defaults to PACKED when
+    every expert matrix given came out of pack_bf16 / pack_mxfp4, else
+    ROWMAJOR; the library refuses bf16 / MXFP4 matrices declared ROWMAJOR."""
+    if layout is None:
+        mats = [m for m in (w_gate, w_up, w_down, sh_gate, sh_up, sh_down) if m is not None]
+        layout = MOE_LAYOUT_PACKED if all(_is_packed(m) for m in mats) else MOE_LAYOUT_ROWMAJOR
+    return _Weights(layout, router_w=router_w, router_bias=router_bias, w_gate=w_gate, w_up=w_up,
                     w_down=w_down, s_gate=s_gate, s_up=s_up, s_down=s_down, sh_gate=sh_gate,
                     sh_up=sh_up, sh_down=sh_down)
 
@@ -166,6 +177,7 @@ def pack_bf16(w, stream=None):
     E, N, K = (1, *w.shape) if w.dim() == 2 else w.shape
     out = torch.empty_like(w)
     moe_pack_bf16(E, N, K, w, out, stream)
+    out._moe_layout = "packed"
     return out
 
 
@@ -182,6 +194,7 @@ def pack_mxfp4(codes, scales, stream=None):
     out_c = torch.empty_like(codes)
     out_s = torch.empty_like(scales)
     moe_pack_mxfp4(E, N, 2 * K2, codes, scales, out_c, out_s, stream)
+    out_c._moe_layout = out_s._moe_layout = "packed"
     return out_c, out_s
 
 

@@ -86,6 +86,18 @@ int check_shape(const moe_shape_t *s)
     return MOE_OK;
 }
 
+// The kernels index token rows, staging rows and logit planes of one pass
+// with 32-bit offsets: refuse passes whose largest offset would not fit.
+int check_pass_size(const moe_shape_t *s, int64_t Tc)
+{
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t rows = Tc * s->top_k + (s->I_shared > 0 ? Tc : 0);
+    const int64_t width = std::max<int64_t>(s->H, std::max(s->I, s->I_shared));
+    if (Tc * s->H >= lim || Tc * s->E * 8 >= lim || rows * width >= lim)
+        return fail(MOE_EINVAL, "pass too large for 32-bit row offsets: lower T or chunk_T");
+    return MOE_OK;
+}
+
 int check_weights(const moe_shape_t *s, const moe_weights_t *w)
 {
     if (!w)
@@ -97,6 +109,13 @@ int check_weights(const moe_shape_t *s, const moe_weights_t *w)
         return fail(MOE_EINVAL, "weight pointer not 16-byte aligned");
     if (w->router_bias && ((uintptr_t)w->router_bias & 3u))
         return fail(MOE_EINVAL, "router_bias not 4-byte aligned");
+    // bf16 / MXFP4 kernels read the packed layouts only; f32 ones row-major
+    const int want = s->w_dtype == MOE_F32 ? MOE_LAYOUT_ROWMAJOR : MOE_LAYOUT_PACKED;
+    if (w->layout != want)
+        return fail(MOE_EINVAL, s->w_dtype == MOE_F32
+                                    ? "f32 expert matrices must be row-major (layout ROWMAJOR)"
+                                    : "bf16/MXFP4 expert matrices must be packed by moe_pack_bf16 / "
+                                      "moe_pack_mxfp4 and declared with layout PACKED");
     if (s->w_dtype == MOE_MXFP4) {
         if (!w->s_gate || !w->s_up || !w->s_down)
             return fail(MOE_EINVAL, "MXFP4 scale pointer is NULL");
@@ -323,7 +342,7 @@ extern "C" {
 
 size_t moe_workspace_bytes(const moe_shape_t *shape)
 {
-    if (check_shape(shape) != MOE_OK)
+    if (check_shape(shape) != MOE_OK || check_pass_size(shape, pass_tokens(shape)) != MOE_OK)
         return 0;
     return layout(shape, pass_tokens(shape)).total;
 }
@@ -345,6 +364,8 @@ int moe_forward(const moe_shape_t *s, const moe_weights_t *w, const void *x, voi
         (topk_w && !aligned16(topk_w)))
         return fail(MOE_EINVAL, "x, y, topk_idx or topk_w not 16-byte aligned");
     const int Tc = pass_tokens(s);
+    if ((rc = check_pass_size(s, Tc)))
+        return rc;
     const Layout L = layout(s, Tc);
     if (!ws || ((uintptr_t)ws & 255u))
         return fail(MOE_EINVAL, "workspace NULL or not 256-byte aligned");
@@ -463,6 +484,8 @@ int moe_route(const moe_shape_t *s, const moe_weights_t *w, const void *x, int32
         return fail(MOE_EINVAL, "x or topk_idx is NULL");
     if (!aligned16(x) || !aligned16(topk_idx) || (topk_w && !aligned16(topk_w)))
         return fail(MOE_EINVAL, "x, topk_idx or topk_w not 16-byte aligned");
+    if ((rc = check_pass_size(s, s->T)))
+        return rc;
     const Layout L = layout(s, s->T);
     if (!ws || ((uintptr_t)ws & 255u))
         return fail(MOE_EINVAL, "workspace NULL or not 256-byte aligned");

@@ -385,9 +385,9 @@ __global__ __launch_bounds__(64 * NW, WF ? 2 : 3) void expert_mxfp4(MxP p, const
         for (int cb = 0; cb < CPW; ++cb) {
             const int n = nw0 + 16 * cb;
             if (GU)
-                p.out[pos * p.ldh + n] = f2bf(silu(acc[0][cb][i]) * acc[NB - 1][cb][i]);
+                p.out[(int64_t)pos * p.ldh + n] = f2bf(silu(acc[0][cb][i]) * acc[NB - 1][cb][i]);
             else
-                p.out[pos * p.H + n] = f2bf(acc[0][cb][i]);
+                p.out[(int64_t)pos * p.H + n] = f2bf(acc[0][cb][i]);
         }
     }
 }

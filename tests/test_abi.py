@@ -62,7 +62,8 @@ class FakeW:
 
     def __init__(self, **over):
         base = 0x7F0000000000
-        d = dict(router_w=base, w_gate=base + 0x1000, w_up=base + 0x2000, w_down=base + 0x3000)
+        d = dict(router_w=base, w_gate=base + 0x1000, w_up=base + 0x2000, w_down=base + 0x3000,
+                 layout=moe.MOE_LAYOUT_PACKED)
         d.update(over)
         self.c = moe.moe_weights_t(**d)
 
@@ -112,6 +113,43 @@ def test_null_and_alignment_errors():
     # MXFP4 without scales, shared expert without weights
     assert call(shape(w="mxfp4")) == moe.MOE_EINVAL
     assert call(shape(I_shared=768)) == moe.MOE_EINVAL
+
+
+def test_weight_layout_must_be_declared():
+    """bf16 and MXFP4 expert matrices are read in the packed layouts only: a
+    struct that declares them row-major (the zero value) is refused, as is an
+    f32 layer declared packed."""
+    assert call(shape(), w=FakeW(layout=moe.MOE_LAYOUT_ROWMAJOR)) == moe.MOE_EINVAL
+    assert "packed" in moe.moe_last_error()
+    assert call(shape(), w=FakeW(layout=7)) == moe.MOE_EINVAL
+    f32 = shape(act="f32", w="f32", H=256, I=128, E=8, top_k=2)
+    assert call(f32, w=FakeW(layout=moe.MOE_LAYOUT_PACKED)) == moe.MOE_EINVAL
+    assert "row-major" in moe.moe_last_error()
+    # the binding declares PACKED only when every matrix came out of the packers
+    import torch
+    t = torch.zeros(4, 64, dtype=torch.bfloat16)
+    assert moe.make_weights(t, t, t, t).c.layout == moe.MOE_LAYOUT_ROWMAJOR
+    p = torch.zeros(4, 64, dtype=torch.bfloat16)
+    p._moe_layout = "packed"
+    assert moe.make_weights(t, p, p, p).c.layout == moe.MOE_LAYOUT_PACKED
+    assert moe.make_weights(t, p, t, p).c.layout == moe.MOE_LAYOUT_ROWMAJOR
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=1 << 20, H=2048),                                 # T*H = 2^31
+    dict(T=50000, H=4096, E=64, top_k=16, I=1024),            # rows*H > 2^31
+    dict(T=300000, H=1024, E=1023, top_k=8, I=256),           # T*E*8 > 2^31
+    dict(T=200000, H=1024, E=64, top_k=8, I=256, I_shared=2048),  # rows*I_shared
+])
+def test_pass_too_large_for_32bit_offsets(kw):
+    """Passes whose token, staging or logit offsets would not fit 32 bits are
+    refused before any launch; chunk_T brings the pass back into range."""
+    sh = 0x7F0000100000
+    w = FakeW(sh_gate=sh, sh_up=sh + 0x1000, sh_down=sh + 0x2000)
+    assert call(shape(**kw), w=w, ws_bytes=1 << 50) == moe.MOE_EINVAL
+    assert "32-bit" in moe.moe_last_error()
+    assert moe.moe_workspace_bytes(shape(**kw)) == 0
+    assert moe.moe_workspace_bytes(shape(**kw, chunk_T=1024)) > 0
 
 
 def test_workspace_too_small():
