@@ -77,6 +77,8 @@ def _load():
         lib.or_topk_margin.argtypes = [P, P, ctypes.c_int, P, P]
         lib.or_permute.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P]
         lib.or_forward.argtypes = [P, P, ctypes.c_int, P, P, P, P]
+        lib.or_set_threads.argtypes = [ctypes.c_int]
+        lib.or_max_threads.argtypes = []
         _lib = lib
     return _lib
 
@@ -202,3 +204,12 @@ def e2m1_value(code: int) -> float:
 
 def e8m0_value(s: int) -> float:
     return _load().or_e8m0_value(s)
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads the oracle uses (timing only: results do not depend on it)."""
+    _check(_load().or_set_threads(int(n)), "set_threads")
+
+
+def max_threads() -> int:
+    return int(_load().or_max_threads())

@@ -32,11 +32,13 @@
  *  - MXFP4 follows the OCP MX v1.0 layout: E2M1 codes, two per byte with the
  *    even element in the low nibble, one E8M0 scale per 32 elements along K.
  *
- * Parity pins for every function live in tests/test_oracle_*.py.
+ * Parity pins for every function live in tests/test_oracle.py (with the
+ * page figures and format tables under tests/golden/).
  */
 #include "moe_oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -68,19 +70,6 @@ double or_e8m0_value(uint8_t s)
     if (s == 0xFF)
         return NAN;
     return ldexp(1.0, (int)s - 127);
-}
-
-void or_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t N,
-                      int64_t K, double *out)
-{
-    for (int64_t n = 0; n < N; ++n) {
-        for (int64_t kk = 0; kk < K; ++kk) {
-            uint8_t byte = codes[n * (K / 2) + kk / 2];
-            uint8_t code = (kk % 2 == 0) ? (byte & 0xF) : (byte >> 4);
-            double s = or_e8m0_value(scales[n * (K / 32) + kk / 32]);
-            out[n * K + kk] = or_e2m1_value(code) * s;
-        }
-    }
 }
 
 /* Element (n, kk) of an [N, K] matrix stored in `dtype`. */
@@ -395,3 +384,15 @@ int or_decode(const void *base, const uint8_t *scales, int dtype, int64_t N,
     decode_matrix(base, scales, dtype, N, K, out);
     return OR_OK;
 }
+
+/* ---- threads (timing only; results do not depend on the count) -------- */
+
+int or_set_threads(int n)
+{
+    if (n < 1)
+        return OR_EINVAL;
+    omp_set_num_threads(n);
+    return OR_OK;
+}
+
+int or_max_threads(void) { return omp_get_max_threads(); }

@@ -39,8 +39,6 @@ typedef struct {
 double or_bf16_to_f64(uint16_t v);
 double or_e2m1_value(uint8_t code);
 double or_e8m0_value(uint8_t s);
-void or_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t N,
-                      int64_t K, double *out);
 int or_decode(const void *base, const uint8_t *scales, int dtype, int64_t N,
               int64_t K, double *out);
 
@@ -61,6 +59,11 @@ int or_permute(int n_tok, int top_k, int E, const int32_t *idx,
 /* y [n_tok, H] for the listed tokens, plus their idx and w (nullable). */
 int or_forward(const or_problem *p, const void *x, int n_tok,
                const int32_t *tokens, double *y, int32_t *idx, double *w);
+
+/* OpenMP threads of the calls above (for timing; results are the same for
+ * every count) and the current count. */
+int or_set_threads(int n);
+int or_max_threads(void);
 
 #ifdef __cplusplus
 }
