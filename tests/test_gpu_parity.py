@@ -1,8 +1,13 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
 Routing indices must match bit-exactly on margin-filtered inputs; y within
-max|y - y_ref| / max|y_ref| <= 2e-2 (bf16 weights), 5e-2 (MXFP4), 1e-4 (fp32).
-Full-size workloads compare every token's routing and a sample of y rows.
+max|y - y_ref| / max|y_ref| <= 2e-2 (bf16 weights), 5e-2 (MXFP4), 1e-4 (fp32),
+and within the tighter self-imposed bars of harness.TIGHT.  Every workload
+compares every token's routing; y is compared on every row except at the
+widest layer (T=8192, 19 GB of weights), where the rows are chosen to include
+the first and last row of every row tile of the most-loaded experts and of
+the shared expert's group.  Every measured error is printed at the end of the
+run (tests/errlog.py).
 """
 import sys
 
@@ -24,6 +29,7 @@ def _gpu_ready():
 if not _gpu_ready():
     pytest.skip("no GPU visible", allow_module_level=True)
 
+import errlog  # noqa: E402
 import harness as hx  # noqa: E402
 import routed_expert_ffn_moe_amd as moe  # noqa: E402
 
@@ -32,6 +38,15 @@ _LAYERS = {}
 
 def say(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def check_err(case, err, w):
+    """Record the measured error and hold it to the stated tolerance and to
+    the tighter self-imposed bar for weight format `w`."""
+    say("[err]", case, err)
+    errlog.record(case, err, hx.TIGHT[w])
+    assert err <= hx.TOL[w], (case, err)
+    assert err <= hx.TIGHT[w], (case, err)
 
 
 def layer(name):
@@ -46,8 +61,32 @@ def layer(name):
     return c, _LAYERS[key]
 
 
-# tokens compared row by row against the oracle (None = all)
-SAMPLE = {"c0": None, "c1": None, "c2": 192, "c3": 48, "c4_t6": None, "c4_t1": None}
+def tile_edge_tokens(idx, E, k, n_shared, bm=128, heavy=3, extra=16, seed=0):
+    """Tokens whose grouped rows sit where row-tile bugs show: for the `heavy`
+    most-loaded experts the first and last row of every row tile of `bm`
+    rows, plus three rows of their third tile; the first and last token of
+    the shared expert's first, second and last tiles (its group holds every
+    token in order); and `extra` seeded random tokens."""
+    counts, offsets, row_src = oracle.permute(idx, E)
+    pick = set()
+    for e in np.argsort(-counts, kind="stable")[:heavy]:
+        o, n = int(offsets[e]), int(counts[e])
+        for t0 in range(0, n, bm):
+            rows = [t0, min(t0 + bm, n) - 1]
+            if t0 == 2 * bm:
+                rows += [t0 + 1, (t0 + min(t0 + bm, n)) // 2]
+            pick.update(int(row_src[o + r]) // k for r in rows if r < n)
+    if n_shared:
+        for t0 in (0, bm, ((n_shared - 1) // bm) * bm):
+            pick.update([t0, min(t0 + bm, n_shared) - 1])
+    rng = np.random.default_rng(seed)
+    pick.update(rng.choice(idx.shape[0], size=extra, replace=False).tolist())
+    return np.array(sorted(pick), dtype=np.int32)
+
+
+# tokens compared row by row against the oracle (None = all; "edges" = the
+# tile-edge selection above)
+SAMPLE = {"c0": None, "c1": None, "c2": None, "c3": "edges", "c4_t6": None, "c4_t1": None}
 
 
 @pytest.mark.parametrize("name", ["c0", "c1", "c4_t6", "c4_t1", "c2", "c3"])
@@ -64,9 +103,11 @@ def test_forward_parity(name):
     assert np.abs(w_h - w_r).max() <= hx.W_TOL
     # y rows
     n = SAMPLE[name]
-    tokens = None if n is None else np.sort(
-        np.random.default_rng(0).choice(c["T"], size=min(n, c["T"]), replace=False)).astype(np.int32)
-    experts = None if name != "c3" else sorted(set(idx_r[tokens].reshape(-1).tolist()))
+    tokens = None if n is None else tile_edge_tokens(idx_r, c["E"], c["top_k"],
+                                                     c["T"] if c["I_shared"] else 0)
+    experts = None if tokens is None else sorted(set(idx_r[tokens].reshape(-1).tolist()))
+    if tokens is not None:
+        say("[parity]", name, "comparing", tokens.size, "rows over", len(experts), "experts")
     L = hx.oracle_layer(c, g.lay, experts)
     y_ref, idx_o, _ = oracle.forward(L, x, tokens)
     yh = hx.y_host(y, c["act"])
@@ -75,9 +116,13 @@ def test_forward_parity(name):
         assert np.array_equal(idx_o, idx_r[tokens])
     err = hx.rel_err(yh, y_ref)
     say("[parity]", name, "rel err", err)
-    print("[parity] %s rel_err=%.3e" % (name, err))
+    errlog.record("forward %s (%s rows)" % (name, "all" if tokens is None else tokens.size),
+                  err, hx.TIGHT[c["w"]])
+    werr = float(np.abs(w_h - w_r).max())
+    errlog.record("routing weights %s (max abs)" % name, werr, hx.W_TOL)
     assert np.isfinite(yh).all()
     assert err <= hx.TOL[c["w"]], err
+    assert err <= hx.TIGHT[c["w"]], err
 
 
 @pytest.mark.parametrize("name,T", [("c1", None), ("c1", 16), ("c1", 129), ("c2", None),
@@ -120,11 +165,14 @@ def test_chunk_invariance(name, chunk):
     assert torch.equal(y0, y1)
 
 
-@pytest.mark.parametrize("name", ["c2", "c4_t6", "c4_t1"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4_t6", "c4_t1"])
 def test_determinism_and_poisoned_workspace(name):
-    """Bit-identical results on a workspace filled with 0xFF (the decode rows'
-    one-launch routing keeps its arrival counter there) and on the same
-    workspace again (a second call finds the first call's counter)."""
+    """Bit-identical results on a workspace filled with 0xFF, NaN in bf16 and
+    fp32 (so a staging row, h row, tile record or counter the kernels failed
+    to write would show), and on the same workspace again (a second call
+    finds the first call's leftovers, such as the short-pass route ticket).
+    T=8192 covers the shared expert's 8,192 extra staging rows, T=128 the
+    short-pass routing with several route workgroups."""
     say("[determinism]", name)
     c, g = layer(name)
     x = hx.margin_x(c, g.lay)
@@ -147,7 +195,7 @@ def test_ragged_and_tiny_T(T):
     y, idx, w = g.forward(hx.act_torch(x, c["act"], "cuda"))
     y_ref, idx_r, _ = oracle.forward(hx.oracle_layer(c, g.lay), x)
     assert np.array_equal(idx.cpu().numpy(), idx_r)
-    assert hx.rel_err(hx.y_host(y, "bf16"), y_ref) <= hx.TOL["bf16"]
+    check_err("ragged T=%d" % T, hx.rel_err(hx.y_host(y, "bf16"), y_ref), "bf16")
 
 
 def test_all_tokens_on_the_same_experts():
@@ -170,7 +218,8 @@ def test_all_tokens_on_the_same_experts():
     assert np.array_equal(idx_h, idx_r)
     tokens = np.arange(0, 300, 7, dtype=np.int32)
     y_ref, _, _ = oracle.forward(hx.oracle_layer(c, lay), x, tokens)
-    assert hx.rel_err(hx.y_host(y, "bf16")[tokens], y_ref) <= hx.TOL["bf16"]
+    check_err("all tokens on 8 experts (T=300)", hx.rel_err(hx.y_host(y, "bf16")[tokens], y_ref),
+              "bf16")
 
 
 @pytest.mark.parametrize("T,hot", [(40, True), (128, False)])
@@ -202,9 +251,8 @@ def test_mxfp4_many_rows(T, hot):
     tokens = np.arange(T, dtype=np.int32) if hot else np.arange(0, T, 4, dtype=np.int32)
     experts = sorted(set(idx_r[tokens].reshape(-1).tolist()))
     y_ref, _, _ = oracle.forward(hx.oracle_layer(c, lay, experts), x, tokens)
-    err = hx.rel_err(hx.y_host(y, c["act"])[tokens], y_ref)
-    say("[mxfp4 rows] rel err", err)
-    assert err <= hx.TOL["mxfp4"], err
+    check_err("mxfp4 T=%d%s" % (T, " hot experts" if hot else ""),
+              hx.rel_err(hx.y_host(y, c["act"])[tokens], y_ref), "mxfp4")
 
 
 @pytest.mark.parametrize("T", [2, 3, 8])
@@ -223,9 +271,62 @@ def test_mxfp4_decode_sizes(T):
     tokens = np.arange(T, dtype=np.int32)
     experts = sorted(set(idx_r.reshape(-1).tolist()))
     y_ref, _, _ = oracle.forward(hx.oracle_layer(c, g.lay, experts), x, tokens)
-    err = hx.rel_err(hx.y_host(y, c["act"]), y_ref)
-    say("[mxfp4 decode] rel err", err)
-    assert err <= hx.TOL["mxfp4"], err
+    check_err("mxfp4 decode T=%d" % T, hx.rel_err(hx.y_host(y, c["act"]), y_ref), "mxfp4")
+
+
+def _dequantised_bf16_layer(c, lay, experts):
+    """A bf16 layer holding exactly the values the MXFP4 layer decodes to
+    (E2M1 code x 2^(s-127) has at most two significant bits, so bf16 holds
+    it exactly), for the experts listed; the other experts are zero (the
+    routing, which reads only the router, is unchanged)."""
+    out = {}
+    for name, N, K in (("w_gate", c["I"], c["H"]), ("w_up", c["I"], c["H"]),
+                       ("w_down", c["H"], c["I"])):
+        codes = getattr(lay, name)
+        scales = getattr(lay, "s_" + name[2:])
+        host = np.zeros((c["E"], N, K), np.uint16)
+        for e in experts:
+            v = oracle.decode(mi.to_host(codes[e]), "mxfp4", N, K, mi.to_host(scales[e]))
+            b = mi.bf16_bits(v.astype(np.float32))
+            assert np.array_equal(oracle.decode(b, "bf16", N, K), v), "not exact in bf16"
+            host[e] = b
+        out[name] = torch.from_numpy(host.view(np.int16)).view(torch.bfloat16).to("cuda")
+    return mi.LayerData(c=dict(c, w="bf16"), router_w=lay.router_w, router_bias=lay.router_bias,
+                        **out)
+
+
+@pytest.mark.parametrize("T,hot", [(6, False), (1, False), (40, True)])
+def test_mxfp4_path_matches_bf16_path_on_the_same_weights(T, hot):
+    """Format errors apart from kernel errors: the MXFP4 kernels (fp4 weights
+    on the scaled MFMA, activations as a hi/lo MXFP8 pair) against the bf16
+    kernels run on the dequantised weights themselves, held to the bf16
+    tolerance; both against the oracle as well.  T=40 with every token on the
+    same 8 experts gives the MXFP4 kernels full 16-row tiles."""
+    say("[fp4 vs bf16] T =", T, "hot" if hot else "")
+    c, g = layer("c4_t6")
+    c = dict(c, T=T, seed=6000 + T)
+    lay = g.lay
+    if hot:
+        bias = np.zeros(c["E"], np.float32)
+        for r, e in enumerate([3, 17, 64, 65, 130, 200, 254, 255]):
+            bias[e] = 100.0 - 10.0 * r
+        lay = mi.LayerData(c=c, router_w=lay.router_w, router_bias=bias, w_gate=lay.w_gate,
+                           w_up=lay.w_up, w_down=lay.w_down, s_gate=lay.s_gate,
+                           s_up=lay.s_up, s_down=lay.s_down)
+    x = hx.margin_x(c, lay)
+    idx_r, _, _ = oracle.route(hx.router_only_layer(c, lay), x)
+    experts = sorted(set(idx_r.reshape(-1).tolist()))
+    xd = hx.act_torch(x, c["act"], "cuda")
+    y4, i4, w4 = hx.GpuLayer(c, lay).forward(xd)
+    cb = dict(c, w="bf16")
+    y16, i16, w16 = hx.GpuLayer(cb, _dequantised_bf16_layer(c, lay, experts)).forward(xd)
+    assert torch.equal(i4, i16) and torch.equal(w4, w16)
+    assert np.array_equal(i4.cpu().numpy(), idx_r)
+    y4h, y16h = hx.y_host(y4, "bf16"), hx.y_host(y16, "bf16")
+    check_err("fp4 vs bf16 kernels, same weights, T=%d" % T, hx.rel_err(y4h, y16h), "bf16")
+    y_ref, _, _ = oracle.forward(hx.oracle_layer(c, lay, experts), x)
+    check_err("mxfp4 vs oracle T=%d (same-weights case)" % T, hx.rel_err(y4h, y_ref), "mxfp4")
+    check_err("bf16 on dequantised weights vs oracle T=%d" % T, hx.rel_err(y16h, y_ref), "bf16")
 
 
 @pytest.mark.parametrize("T", [5, 100])
@@ -243,9 +344,8 @@ def test_shared_expert_short_passes(T):
     tokens = np.unique(np.linspace(0, T - 1, 6).astype(np.int32))
     experts = sorted(set(idx_r[tokens].reshape(-1).tolist()))
     y_ref, _, _ = oracle.forward(hx.oracle_layer(c, g.lay, experts), x, tokens)
-    err = hx.rel_err(hx.y_host(y, c["act"])[tokens], y_ref)
-    say("[shared short] rel err", err)
-    assert err <= hx.TOL[c["w"]], err
+    check_err("shared expert T=%d" % T, hx.rel_err(hx.y_host(y, c["act"])[tokens], y_ref),
+              c["w"])
 
 
 # Small layers whose shapes take the other kernel variants: the router
@@ -276,9 +376,7 @@ def test_shape_sweep(name):
     y_ref, idx_r, w_r = oracle.forward(hx.oracle_layer(c, lay), x)
     assert np.array_equal(idx.cpu().numpy(), idx_r)
     assert np.abs(w.cpu().numpy() - w_r).max() <= hx.W_TOL
-    err = hx.rel_err(hx.y_host(y, c["act"]), y_ref)
-    say("[sweep]", name, "rel err", err)
-    assert err <= hx.TOL[c["w"]], err
+    check_err("sweep %s" % name, hx.rel_err(hx.y_host(y, c["act"]), y_ref), c["w"])
 
 
 def test_zero_tokens_is_a_no_op():
