@@ -29,26 +29,40 @@ PEAK_TFLOPS = {"bf16": 2500.0, "mxfp4": 10100.0, "f32": 157.3}
 MALL_BYTES = 256 << 20
 
 
-def stage_work(c, counts):
-    """Algorithmic bytes and flops of each stage for one call: every operand
-    read once, every output written once; expert weights only for the experts
-    that received tokens."""
+def stage_work(c, counts, fused_down_combine=False):
+    """Algorithmic bytes and flops of each stage for one call: the operands
+    the method itself must read and the outputs it must write, each once;
+    expert weights only for the experts that received tokens (Es).  Over the
+    whole layer the bytes add up to Es*3*H*I*b_w + E*H*b_r + 3*H*I_s*b_w +
+    T*H*(b_x + b_y) + 8*T*k.  The intermediate h rows, the per-pair staging
+    rows and the permutation's index arrays are the implementation's own
+    traffic: `_overhead` gives their bytes (written once and read once),
+    reported beside the algorithmic figure, never inside it.  With
+    `fused_down_combine` (MXFP4 decode rows) y is written by the down stage."""
     T, H, E, k, I, Is = c["T"], c["H"], c["E"], c["top_k"], c["I"], c["I_shared"]
     a = 4 if c["act"] == "f32" else 2
     bw = {"f32": 4.0, "bf16": 2.0, "mxfp4": 17.0 / 32.0}[c["w"]]
     Es = int((counts > 0).sum())
     pairs = T * k
     rows = pairs + (T if Is else 0)
+    y_bytes = T * H * a
     return {
         "router": (T * H * a + E * H * a + (E * 4 if c["bias"] else 0) + pairs * 8,
                    2.0 * T * H * E),
-        "permute": (pairs * 4 * 3, 0.0),
-        "gate_up": (Es * 2 * I * H * bw + 2 * Is * H * a + T * H * a + pairs * I * a + T * Is * a,
+        "permute": (0.0, 0.0),
+        "gate_up": (Es * 2 * I * H * bw + 2 * Is * H * a + T * H * a,
                     4.0 * pairs * H * I + 4.0 * T * H * Is),
-        "down": (Es * H * I * bw + H * Is * a + pairs * I * a + T * Is * a + rows * H * a,
+        "down": (Es * H * I * bw + H * Is * a + (y_bytes if fused_down_combine else 0),
                  2.0 * pairs * H * I + 2.0 * T * H * Is),
-        "combine": (rows * H * a + T * H * a, float(rows * H)),
+        "combine": (0.0 if fused_down_combine else y_bytes, float(rows * H)),
         "_Es": Es,
+        # the layer reads x once (router and gate+up each count it above)
+        "_layer": (Es * 3 * H * I * bw + E * H * a + (E * 4 if c["bias"] else 0)
+                   + 3 * H * Is * a + T * H * 2 * a + pairs * 8,
+                   2.0 * T * H * E + 6.0 * pairs * H * I + 6.0 * T * H * Is),
+        "_overhead": {"h": 2 * (pairs * I + T * Is) * a,
+                      "staging": 0 if fused_down_combine else 2 * rows * H * a,
+                      "permutation": pairs * 4 * 3},
     }
 
 
@@ -89,24 +103,52 @@ def measured_traffic(workload, stage):
 
 
 def roofline(work, stage, ms, dtype):
+    """The stage against the resource that bounds it: algorithmic bytes over
+    8 TB/s or flops over the dense MFMA peak of its dtype, whichever takes
+    longer at peak; `achieved` is that figure per second of the measured
+    stage time."""
     byts, flops = work[stage]
     dur = ms / 1e3
     t_hbm = byts / (PEAK_HBM_GBS * 1e9)
     t_mma = flops / (PEAK_TFLOPS[dtype] * 1e12)
+    common = {"traffic": None, "kernel": stage, "avg_us": round(ms * 1e3, 2),
+              "alg_bytes": int(byts), "alg_flops": flops}
     if t_mma > t_hbm:
         ach = flops / dur / 1e12
         return {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_TFLOPS[dtype],
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS[dtype], 4), "traffic": None,
-                "kernel": stage, "avg_us": round(ms * 1e3, 2), "alg_bytes": int(byts),
-                "alg_flops": flops}
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS[dtype], 4), **common}
     ach = byts / dur / 1e9
     return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": stage,
-            "avg_us": round(ms * 1e3, 2), "alg_bytes": int(byts), "alg_flops": flops}
+            "frac": round(ach / PEAK_HBM_GBS, 4), **common}
+
+
+def mfma_frac(work, stage, ms, dtype):
+    """Useful matrix flops of the stage per second against the dense peak of
+    its dtype (padding rows not counted)."""
+    return round(work[stage][1] / (ms / 1e3) / 1e12 / PEAK_TFLOPS[dtype], 4)
+
+
+def layer_roofline(work, ms_step, dtype):
+    """The whole layer call against its roofline: the layer's algorithmic
+    bytes at 8 TB/s or its flops at the MFMA peak, whichever is longer."""
+    byts, flops = work["_layer"]
+    t_roof = max(byts / (PEAK_HBM_GBS * 1e9), flops / (PEAK_TFLOPS[dtype] * 1e12))
+    return {"alg_bytes": int(byts), "alg_flops": flops, "roofline_us": round(t_roof * 1e6, 2),
+            "measured_us": round(ms_step * 1e3, 2), "frac": round(t_roof / (ms_step / 1e3), 4)}
+
+
+def weight_sets(c):
+    """Independent weight sets to rotate through so that consecutive calls
+    find their expert weights in HBM, not in the 256 MB infinity cache: one
+    when a call touches more than twice that, else enough sets (at most 16)
+    to exceed it twice over."""
+    per_call = min(c["top_k"] * c["T"], c["E"]) * 3 * c["H"] * c["I"] * (
+        17.0 / 32.0 if c["w"] == "mxfp4" else 2)
+    return 1 if per_call > 2 * MALL_BYTES else int(min(16, 2 * MALL_BYTES // max(per_call, 1) + 1))
 
 
 class Workload:
-    def __init__(self, name, wsets=1, dev="cuda", keep_rowmajor=False):
+    def __init__(self, name, wsets=None, dev="cuda", keep_rowmajor=False, cfg=None):
         import torch
 
         import moe_inputs as mi
@@ -114,8 +156,10 @@ class Workload:
         self.torch, self.moe = torch, moe
         self.name = name
         self.keep_rowmajor = keep_rowmajor
-        self.c = mi.cfg(name)
+        self.c = dict(cfg) if cfg is not None else mi.cfg(name)
         c = self.c
+        if wsets is None:
+            wsets = weight_sets(c)
         self.layers = [mi.make_layer(c, dev, s) for s in range(wsets)]
         x = mi.make_x(c)
         self.x_host = x
@@ -221,10 +265,11 @@ class Workload:
 
 
 def ceilings():
-    """Measured ceilings of this device, beside the published peaks: the HBM
-    read rate (moe_probe_read over a 2 GiB buffer, eight times the infinity
-    cache) and the sustained bf16 MFMA rate (moe_probe_mfma, 2 waves per SIMD
-    of 8 independent 16x16x32 chains); best of 5 timed runs each."""
+    """Measured ceilings of this device, beside the published peaks (context
+    only: the roofline fractions are taken against the published peaks): the
+    HBM read rate (moe_probe_read over a 2 GiB buffer, eight times the
+    infinity cache) and the sustained bf16 MFMA rate (moe_probe_mfma, 2 waves
+    per SIMD of 8 independent 16x16x32 chains); best of 5 timed runs each."""
     import torch
 
     import routed_expert_ffn_moe_amd as moe
@@ -256,18 +301,22 @@ def ceilings():
             "probes": "moe_probe_read over 2 GiB; moe_probe_mfma, %d waves x %d rounds" % (waves, iters)}
 
 
-def with_ceiling(roof, ceil):
-    """The roofline entry plus the fraction of the measured ceiling."""
-    m = ceil["hbm_read_GBps"] if roof["bound"] == "hbm" else (
-        ceil["bf16_mfma_TFLOPs"] if roof["unit"] == "TFLOP/s" and roof["peak"] == PEAK_TFLOPS["bf16"]
-        else None)
-    if m:
-        roof = dict(roof, measured_ceiling=m, frac_of_measured=round(roof["achieved"] / m, 4))
-    return roof
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(wl, seconds):
-    """The CPU oracle (as it stands) on a sample of the workload's tokens."""
+    """The CPU oracle (as it stands: plain C, fp64, one token at a time, OpenMP
+    over tokens) on seeded samples of the workload's tokens, with all host
+    threads and with one; each figure the median of three timed samples
+    sized to about a third of `seconds`."""
     import numpy as np
 
     import moe_inputs as mi
@@ -281,19 +330,115 @@ def cpu_baseline(wl, seconds):
                      sh_gate=h(lay.sh_gate), sh_up=h(lay.sh_up), sh_down=h(lay.sh_down))
     x = wl.x_host
     rng = np.random.default_rng(0)
-    n = 16
-    t0 = time.perf_counter()
-    oracle.forward(L, x, np.sort(rng.choice(c["T"], n, replace=False)).astype(np.int32))
-    dt = time.perf_counter() - t0
-    n = int(min(c["T"], max(n, n * seconds / max(dt, 1e-3))))
-    tok = np.sort(rng.choice(c["T"], n, replace=False)).astype(np.int32)
-    t0 = time.perf_counter()
-    oracle.forward(L, x, tok)
-    dt = time.perf_counter() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": "%d of the %d tokens of the workload (seeded), full layer per token, "
-                      "%.1f s" % (n, c["T"], dt)}
+    all_threads = oracle.max_threads()
+
+    def rate(threads, budget):
+        oracle.set_threads(threads)
+        n = max(1, min(c["T"], threads))
+        t0 = time.perf_counter()
+        oracle.forward(L, x, np.sort(rng.choice(c["T"], n, replace=False)).astype(np.int32))
+        dt = time.perf_counter() - t0
+        n = int(min(c["T"], max(n, n * budget / max(dt, 1e-3))))
+        runs = []
+        for _ in range(3):
+            tok = np.sort(rng.choice(c["T"], n, replace=False)).astype(np.int32)
+            t0 = time.perf_counter()
+            oracle.forward(L, x, tok)
+            runs.append(n / (time.perf_counter() - t0))
+        return n, sorted(runs)[1], runs
+
+    n_all, v_all, r_all = rate(all_threads, seconds / 6)
+    n_one, v_one, r_one = rate(1, seconds / 6)
+    oracle.set_threads(all_threads)
+    return {"value": round(v_all, 2), "unit": "tokens/s", "cores": all_threads, "kind": "oracle",
+            "sample": "median of 3 samples of %d of the %d tokens (seeded), full layer per token, "
+                      "%d threads" % (n_all, c["T"], all_threads),
+            "one_thread": {"value": round(v_one, 2), "unit": "tokens/s",
+                           "sample": "median of 3 samples of %d tokens, 1 thread" % n_one,
+                           "runs": [round(v, 2) for v in r_one]},
+            "runs": [round(v, 2) for v in r_all],
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def describe(wl, wall, stages, steps, graph_wall=None):
+    """Throughput, stage times, roofline of the dominant stage and of the
+    whole layer for one workload's timing."""
+    c = wl.c
+    counts = wl.counts()
+    fused = stages.get("combine", 0.0) == 0.0
+    work = stage_work(c, counts, fused_down_combine=fused)
+    dom = max(stages, key=lambda k: stages[k])
+    ms_step = wall / steps * 1e3
+    gemm = {k: {"us": round(stages[k] * 1e3, 2),
+                "frac_hbm": roofline(work, k, stages[k], c["w"])["frac"]
+                if work[k][0] else None,
+                "frac_mfma_useful": mfma_frac(work, k, stages[k], c["w"])}
+            for k in ("gate_up", "down")}
+    out = {"tokens_per_s": round(c["T"] / (ms_step / 1e3), 1),
+           "us_per_step": round(ms_step * 1e3, 2),
+           "weight_sets": len(wl.weights), "experts_touched": work["_Es"],
+           "max_rows_per_expert": int(counts.max()),
+           "stages_us": {k: round(v * 1e3, 2) for k, v in stages.items()},
+           "roofline": dict(roofline(work, dom, stages[dom], c["w"]),
+                            traffic=measured_traffic(wl.name, dom)),
+           "layer": layer_roofline(work, ms_step, c["w"]),
+           "grouped_gemms": gemm,
+           "overhead_bytes": work["_overhead"]}
+    if graph_wall is not None:
+        out["graph_us_per_step"] = round(graph_wall / steps * 1e6, 2)
+        out["graph_tokens_per_s"] = round(c["T"] / (graph_wall / steps), 1)
+    return out
+
+
+SWEEP_T = (128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768)
+
+
+def sweep(steps, warmup, Ts=SWEEP_T):
+    """Tokens/s of the T=128 prefill layer (H=2048, 256 experts top-8,
+    I=768, bf16, no routing bias) over chunk sizes T, on one weight set and one
+    token set (the first T rows of the largest chunk), and the knee of its
+    per-token cost: the smallest T whose cost is within 5% of the largest
+    chunk's, with the quantum that puts that many tokens on each expert,
+    quantum = tokens per expert x E / k."""
+    import moe_inputs as mi
+    torch = __import__("torch")
+    c0 = mi.cfg("c1")
+    wl = Workload("c1", wsets=1, cfg=dict(c0, T=max(Ts)))
+    x_all = wl.x
+    points = []
+    for T in Ts:
+        wl.c = dict(c0, T=T)
+        wl.x = x_all[:T]
+        wl.shape = wl.moe.make_shape(T, c0["H"], c0["E"], c0["top_k"], c0["I"], 0, 0,
+                                     c0["act"], c0["w"])
+        nb = wl.moe.moe_workspace_bytes(wl.shape)
+        if wl.ws.numel() < nb:
+            wl.ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        wl.y = torch.empty_like(wl.x)
+        wl.idx = torch.empty((T, c0["top_k"]), dtype=torch.int32, device="cuda")
+        wl.w = torch.empty((T, c0["top_k"]), dtype=torch.float32, device="cuda")
+        n = max(5, min(steps, int(4e5 / T)))
+        wall, stages = wl.time(n, warmup)
+        d = describe(wl, wall, stages, n)
+        points.append({"T": T, "tokens_per_s": d["tokens_per_s"], "us_per_step": d["us_per_step"],
+                       "us_per_token": round(d["us_per_step"] / T, 4),
+                       "tokens_per_expert": T * c0["top_k"] / c0["E"],
+                       "experts_touched": d["experts_touched"],
+                       "layer_frac": d["layer"]["frac"],
+                       "gate_up_frac_hbm": d["grouped_gemms"]["gate_up"]["frac_hbm"],
+                       "gate_up_frac_mfma": d["grouped_gemms"]["gate_up"]["frac_mfma_useful"],
+                       "bound": d["roofline"]["bound"]})
+    del wl
+    torch.cuda.empty_cache()
+    floor = points[-1]["us_per_token"]
+    knee = next(p for p in points if p["us_per_token"] <= 1.05 * floor)
+    tpe = knee["tokens_per_expert"]
+    return {"layer": "H=2048 E=256 top-8 I=768 bf16, no routing bias", "points": points,
+            "knee": {"rule": "smallest T with per-token cost within 5%% of T=%d's" % Ts[-1],
+                     "T": knee["T"], "tokens_per_expert": tpe,
+                     "quantum_for_layer": int(round(tpe * c0["E"] / c0["top_k"])),
+                     "quantum_E256_k6": int(round(tpe * 256 / 6)),
+                     "quantum_E128_k8": int(round(tpe * 128 / 8))}}
 
 
 def main():
@@ -304,8 +449,10 @@ def main():
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--extra", default="c1,c3,c4_t6,c4_t1",
                     help="comma-separated secondary workloads ('' for none)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the chunk-size sweep")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the ceiling probes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (calibrates HBM "
                          "byte counters) and exit")
@@ -327,69 +474,61 @@ def main():
     import routed_expert_ffn_moe_amd as moe
     moe.load()
     torch.cuda.set_device(0)
-    ceil = ceilings()
+    ceil = None if args.no_ceilings else ceilings()
 
     wl = Workload(args.workload)
-    wall, stages = wl.time(args.steps, args.warmup)
     c = wl.c
-    ms_step = wall / args.steps * 1e3
-    counts = wl.counts()
-    work = stage_work(c, counts)
-    dom = max((k for k in stages), key=lambda k: stages[k])
+    steps = max(args.steps, 200 if c["T"] <= 8 else args.steps)
+    wall, stages = wl.time(steps, args.warmup)
+    gwall = wl.time_graph(steps, args.warmup) if c["T"] <= 16 else None
+    d = describe(wl, wall, stages, steps, gwall)
+    ms_step = wall / steps * 1e3
     out = {
         "metric": METRIC,
         "value": round(c["T"] / (ms_step / 1e3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": c["w"] if c["w"] != "bf16" else "bf16",
+        "dtype": c["w"],
         "data": "synthetic (seeded inputs, random-init weights)",
         "config": {"workload": c["desc"], "T": c["T"], "H": c["H"], "E": c["E"],
                    "top_k": c["top_k"], "I": c["I"], "I_shared": c["I_shared"],
-                   "bias": c["bias"], "experts_touched": work["_Es"],
-                   "max_rows_per_expert": int(counts.max())},
-        "roofline": with_ceiling(dict(roofline(work, dom, stages[dom], c["w"]),
-                                      traffic=measured_traffic(args.workload, dom)), ceil),
+                   "bias": c["bias"], "experts_touched": d["experts_touched"],
+                   "max_rows_per_expert": d["max_rows_per_expert"]},
+        "roofline": d["roofline"],
+        "layer_roofline": d["layer"],
+        "grouped_gemms": d["grouped_gemms"],
+        "overhead_bytes": d["overhead_bytes"],
+        "stages_us": d["stages_us"],
+        "weight_sets": d["weight_sets"],
         "ceilings": ceil,
-        "stages_us": {k: round(v * 1e3, 2) for k, v in stages.items()},
         "tuning": {k: v for k, v in os.environ.items() if k.startswith("MOE_")},
     }
+    if gwall is not None:
+        out["graph_us_per_step"] = d["graph_us_per_step"]
     also = {}
     del wl
     torch.cuda.empty_cache()
+    import moe_inputs as mi
     for name in [s for s in args.extra.split(",") if s]:
-        import moe_inputs as mi
-        cc = mi.cfg(name)
-        # weight sets rotated so that the touched weights exceed the MALL
-        per_call = cc["top_k"] * cc["T"] * 3 * cc["H"] * cc["I"] * (0.53 if cc["w"] == "mxfp4" else 2)
-        wsets = 1 if per_call > 2 * MALL_BYTES else int(min(16, 2 * MALL_BYTES // max(per_call, 1) + 1))
-        w2 = Workload(name, wsets=wsets)
-        steps = max(args.steps, 200 if cc["T"] <= 8 else args.steps)
-        wall2, st2 = w2.time(steps, args.warmup)
-        cn = w2.counts()
-        wk = stage_work(cc, cn)
-        d2 = max(st2, key=lambda k: st2[k])
-        entry = {}
-        if cc["T"] <= 16:
-            gwall = w2.time_graph(steps, args.warmup)
-            entry = {"graph_tokens_per_s": round(cc["T"] / (gwall / steps), 1),
-                     "graph_us_per_step": round(gwall / steps * 1e6, 2)}
-        also[name] = {"workload": cc["desc"], "tokens_per_s": round(cc["T"] / (wall2 / steps), 1),
-                      "us_per_step": round(wall2 / steps * 1e6, 2), **entry, "weight_sets": wsets,
-                      "experts_touched": wk["_Es"],
-                      "stages_us": {k: round(v * 1e3, 2) for k, v in st2.items()},
-                      "roofline": with_ceiling(dict(roofline(wk, d2, st2[d2], cc["w"]),
-                                                    traffic=measured_traffic(name, d2)), ceil)}
+        w2 = Workload(name)
+        cc = w2.c
+        st = max(args.steps, 200 if cc["T"] <= 8 else args.steps)
+        wall2, st2 = w2.time(st, args.warmup)
+        g2 = w2.time_graph(st, args.warmup) if cc["T"] <= 16 else None
+        also[name] = {"workload": mi.cfg(name)["desc"], **describe(w2, wall2, st2, st, g2)}
         del w2
         torch.cuda.empty_cache()
     out["also"] = also
+    if not args.no_sweep:
+        out["sweep"] = sweep(args.steps, args.warmup)
     if not args.no_cpu_baseline:
-        wl = Workload(args.workload, keep_rowmajor=True)
+        wl = Workload(args.workload, keep_rowmajor=True, wsets=1)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

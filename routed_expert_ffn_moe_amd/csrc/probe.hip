@@ -1,8 +1,9 @@
 // Measurement aids: the ceilings the layer's kernels are compared with on
 // the device they run on (not part of the layer's computation).
 //
-//  probe_read: every CU streams 16-byte loads over a buffer (grid-stride,
-//              8 loads in flight per thread) and discards the data: the
+//  probe_read: every CU streams 16-byte non-temporal loads over a buffer
+//              (grid-stride, four workgroups per CU, 8 loads in flight per
+//              thread) and discards the data: the
 //              achievable HBM read rate for a buffer far larger than the
 //              caches.
 //  probe_mfma: each wave runs 8 independent chains of bf16 16x16x32 MFMAs
@@ -27,7 +28,11 @@ __global__ __launch_bounds__(256) void probe_read(const uint4 *__restrict__ src,
 #pragma unroll
         for (int j = 0; j < PR_NL; ++j) {
             const size_t i = base + (size_t)j * 256;
-            v[j] = i < n16 ? src[i] : uint4{0, 0, 0, 0};
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            // streamed once: non-temporal, as the expert weights are read
+            const u32x4 t = i < n16 ? __builtin_nontemporal_load((const u32x4 *)(src + i))
+                                    : u32x4{0, 0, 0, 0};
+            v[j] = uint4{t[0], t[1], t[2], t[3]};
         }
 #pragma unroll
         for (int j = 0; j < PR_NL; ++j)
@@ -67,7 +72,8 @@ __global__ __launch_bounds__(256) void probe_mfma(int iters, int *__restrict__ s
 
 void launch_probe_read(const void *buf, size_t bytes, int *sink, hipStream_t st)
 {
-    probe_read<<<512, 256, 0, st>>>((const uint4 *)buf, bytes / 16, sink);
+    // four workgroups per CU of the 256, 8 loads of 16 bytes in flight per thread
+    probe_read<<<1024, 256, 0, st>>>((const uint4 *)buf, bytes / 16, sink);
 }
 
 void launch_probe_mfma(int waves, int iters, int *sink, hipStream_t st)

@@ -23,21 +23,43 @@ def _counts(E, touched):
 
 def test_gate_up_bytes_of_the_prefill_layer():
     """T=2048, H=2048, I=768, top-8 bf16 with 102 experts touched: the
-    weights of 102 experts (2 x 768 x 2048 bf16 each, 641,728,512 bytes), x
-    once (8,388,608) and h once (16,384 rows x 768 bf16, 25,165,824)."""
+    weights of 102 experts (2 x 768 x 2048 bf16 each, 641,728,512 bytes) and
+    x once (8,388,608); the h rows (16,384 x 768 bf16) are the
+    implementation's own traffic, reported apart."""
     w = bench.stage_work(mi.cfg("c2"), _counts(256, 102))
     assert w["_Es"] == 102
-    assert w["gate_up"][0] == 641_728_512 + 8_388_608 + 25_165_824
+    assert w["gate_up"][0] == 641_728_512 + 8_388_608
     assert w["gate_up"][1] == 4.0 * 2048 * 8 * 2048 * 768  # 2 GEMMs x 2 flops per MAC
-    # down: 102 experts' 2048 x 768 weights, h read, 16,384 staging rows written
-    assert w["down"][0] == 102 * 2048 * 768 * 2 + 16_384 * 768 * 2 + 16_384 * 2048 * 2
+    # down: 102 experts' 2048 x 768 weights; y is the combine's
+    assert w["down"][0] == 102 * 2048 * 768 * 2
+    assert w["combine"][0] == 2048 * 2048 * 2
+    assert w["_overhead"]["h"] == 2 * 16_384 * 768 * 2
+    assert w["_overhead"]["staging"] == 2 * 16_384 * 2048 * 2
+
+
+def test_layer_bytes_are_the_papers_sum():
+    """The stages add up to Es*3*H*I*b_w + E*H*b_r + 3*H*I_s*b_w + T*H*(b_x +
+    b_y) + 8*T*k: hand count for the wide layer with a shared expert."""
+    c = mi.cfg("c3")
+    w = bench.stage_work(c, _counts(384, 384))
+    T, H, E, k, I, Is = 8192, 4096, 384, 6, 2048, 2048
+    want = 384 * 3 * H * I * 2 + E * H * 2 + E * 4 + 3 * H * Is * 2 + T * H * 4 + 8 * T * k
+    assert w["_layer"][0] == want
+    # the stages' own figures differ only by x, which router and gate+up both read
+    got = sum(v[0] for kk, v in w.items() if not kk.startswith("_"))
+    assert got == want + T * H * 2
+    r = bench.layer_roofline(w, 5.0, "bf16")
+    assert r["roofline_us"] == pytest.approx(want / 8e12 * 1e6, rel=1e-4)
 
 
 def test_mxfp4_weight_bytes_include_the_scales():
     """MXFP4: 16 code bytes and one scale byte per 32 weights (17/32 byte);
-    the decode row touches 8 experts: 13,369,344 weight bytes."""
-    w = bench.stage_work(mi.cfg("c4_t1"), _counts(256, 8))
-    assert w["gate_up"][0] == 13_369_344 + 2048 * 2 + 8 * 768 * 2
+    the decode row touches 8 experts: 13,369,344 weight bytes; with the
+    fused down+combine kernel y is written by the down stage."""
+    w = bench.stage_work(mi.cfg("c4_t1"), _counts(256, 8), fused_down_combine=True)
+    assert w["gate_up"][0] == 13_369_344 + 2048 * 2
+    assert w["down"][0] == 6_684_672 + 2048 * 2
+    assert w["combine"][0] == 0
 
 
 def test_roofline_picks_the_binding_resource():
@@ -45,12 +67,26 @@ def test_roofline_picks_the_binding_resource():
     w = bench.stage_work(c, _counts(256, 102))
     r = bench.roofline(w, "gate_up", 0.17872, "bf16")  # 178.72 us
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
-    assert r["achieved"] == pytest.approx(675_282_944 / 178.72e-6 / 1e9, rel=1e-4)
+    assert r["achieved"] == pytest.approx(650_117_120 / 178.72e-6 / 1e9, rel=1e-4)
     assert r["frac"] == pytest.approx(r["achieved"] / 8000.0, abs=1e-4)
+    assert bench.mfma_frac(w, "gate_up", 0.17872, "bf16") == pytest.approx(
+        103079215104.0 / 178.72e-6 / 2.5e15, abs=1e-4)
     # a stage whose matrix time exceeds its memory time is reported on MFMA
     m = bench.roofline({"x": (1.0e6, 1.0e13)}, "x", 10.0, "bf16")
     assert m["bound"] == "mfma" and m["unit"] == "TFLOP/s"
     assert m["achieved"] == pytest.approx(1000.0) and m["frac"] == pytest.approx(0.4)
+
+
+def test_weight_sets_exceed_the_infinity_cache():
+    """Decode shapes rotate weight sets until the touched weights of the
+    rotation exceed twice the 256 MB infinity cache; prefill layers use one."""
+    for name in ("c4_t1", "c4_t6"):
+        c = mi.cfg(name)
+        n = bench.weight_sets(c)
+        per = min(c["T"] * c["top_k"], c["E"]) * 3 * c["H"] * c["I"] * 17 / 32
+        assert 1 < n <= 16 and (n * per > 2 * bench.MALL_BYTES or n == 16)
+    assert bench.weight_sets(mi.cfg("c2")) == 1
+    assert bench.weight_sets(mi.cfg("c3")) == 1
 
 
 def test_traffic_records_only_for_the_current_sources(tmp_path, monkeypatch):
