@@ -61,6 +61,15 @@ def load() -> ctypes.CDLL:
         path = lib_path()
         if not os.path.exists(path):
             raise RuntimeError("libmoe.so is not built: run `python -m routed_expert_ffn_moe_amd.build`")
+        # torch ships its own HIP runtime (file libamdhip64.so, soname
+        # libamdhip64.so.7).  Loaded first, it is the one libmoe.so binds to.
+        # Loaded after libmoe.so, torch would bring a second runtime into the
+        # process beside ROCm's, and the two cannot both own the device: the
+        # library's calls would then fail with "no ROCm-capable device".
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         lib.moe_workspace_bytes.restype = ctypes.c_size_t
