@@ -147,6 +147,27 @@ int moe_forward(const moe_shape_t *shape, const moe_weights_t *w,
                 const void *x, void *y, int32_t *topk_idx, float *topk_w,
                 void *ws, size_t ws_bytes, void *stream);
 
+/* Bytes of the static device scratch moe_forward_noalloc uses (per GPU). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/* moe_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops and harnesses that must not call
+ * hipMalloc.  Same arguments and results as moe_forward, without the
+ * workspace: the scratch comes from a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES (64 MiB) that each GPU the library runs on holds
+ * from the library's first use there until the process ends; its address on
+ * a device is looked up on the first call on that device.  Allocates nothing
+ * (no hipMalloc/hipFree, no allocating library routine).  A shape whose pass
+ * (min(T, chunk_T) tokens) needs more scratch than that is refused with
+ * MOE_EWORKSPACE before anything is launched (moe_workspace_bytes gives the
+ * need; a smaller chunk_T lowers it: 52 MiB for 1024 tokens at H=2048, E=256,
+ * top-8, I=768).  Every call on a GPU shares that GPU's scratch and leaves
+ * its contents behind (no call needs it cleared): calls that overlap on one
+ * GPU, from several streams or threads, race. */
+int moe_forward_noalloc(const moe_shape_t *shape, const moe_weights_t *w,
+                        const void *x, void *y, int32_t *topk_idx, float *topk_w,
+                        void *stream);
+
 /* Router and permutation only (analysis / test export).  For the tokens of
  * one pass (chunk_T must be 0 or >= T): topk_idx [T, k], topk_w [T, k],
  * counts [E] (pairs per expert), offsets [E+1] (exclusive prefix of counts)

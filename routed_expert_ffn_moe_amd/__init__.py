@@ -17,7 +17,8 @@ from typing import Optional
 __all__ = [
     "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_LAYOUT_ROWMAJOR", "MOE_LAYOUT_PACKED", "MOE_OK",
     "MOE_EINVAL", "MOE_EWORKSPACE", "MOE_EUNSUPPORTED", "MOE_EHIP", "MoeError", "moe_shape_t", "moe_weights_t", "make_shape",
-    "make_weights", "moe_workspace_bytes", "moe_forward", "moe_route", "moe_strerror",
+    "make_weights", "moe_workspace_bytes", "moe_forward", "moe_forward_noalloc",
+    "MOE_NOALLOC_SCRATCH_BYTES", "moe_route", "moe_strerror",
     "moe_last_error", "moe_stage_timing_enable", "moe_stage_timing_read", "moe_pack_bf16",
     "pack_bf16", "moe_pack_mxfp4", "pack_mxfp4", "STAGES", "moe_probe_read", "moe_probe_mfma",
     "lib_path", "load",
@@ -76,6 +77,8 @@ def load() -> ctypes.CDLL:
         lib.moe_workspace_bytes.argtypes = [P]
         lib.moe_forward.restype = ctypes.c_int
         lib.moe_forward.argtypes = [P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.moe_forward_noalloc.restype = ctypes.c_int
+        lib.moe_forward_noalloc.argtypes = [P, P, P, P, P, P, P]
         lib.moe_route.restype = ctypes.c_int
         lib.moe_route.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.moe_strerror.restype = ctypes.c_char_p
@@ -163,6 +166,15 @@ def moe_forward(shape, weights, x, y, topk_idx, topk_w, ws, ws_bytes=None, strea
     _check(load().moe_forward(ctypes.byref(shape), ctypes.byref(weights.c), _ptr(x), _ptr(y),
                               _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws_bytes,
                               _stream(stream)))
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_forward_noalloc(shape, weights, x, y, topk_idx, topk_w, stream=None) -> None:
+    """moe_forward on the library's static device scratch (allocates nothing)."""
+    _check(load().moe_forward_noalloc(ctypes.byref(shape), ctypes.byref(weights.c), _ptr(x),
+                                      _ptr(y), _ptr(topk_idx), _ptr(topk_w), _stream(stream)))
 
 
 def moe_route(shape, weights, x, topk_idx, topk_w, counts, offsets, row_src, ws, ws_bytes=None,

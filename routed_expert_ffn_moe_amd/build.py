@@ -17,8 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["probe.hip", "router.hip", "route_small.hip", "permute.hip", "expert_gemm.hip", "expert_stream.hip", "mxfp4.hip",
-           "moe_api.cpp"]
+SOURCES = ["probe.hip", "router.hip", "route_small.hip", "permute.hip", "expert_gemm.hip",
+           "expert_stream.hip", "mxfp4.hip", "moe_api.cpp", "noalloc.hip"]
 
 FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",

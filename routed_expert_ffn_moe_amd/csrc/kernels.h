@@ -135,6 +135,10 @@ void launch_combine(const CombineArgs &a, hipStream_t st);
 // (packed_bf16_off in common.h).
 void launch_pack_bf16(int E, int N, int K, const uint16_t *w, uint16_t *out, hipStream_t st);
 
+// Records `what` as the calling thread's last error (moe_last_error) and
+// returns `code`: for entry points outside moe_api.cpp.
+int api_fail(int code, const char *what);
+
 // Measurement aids (probe.hip): the device's HBM read and bf16 MFMA ceilings.
 void launch_probe_read(const void *buf, size_t bytes, int *sink, hipStream_t st);
 void launch_probe_mfma(int waves, int iters, int *sink, hipStream_t st);

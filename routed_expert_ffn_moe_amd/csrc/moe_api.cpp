@@ -338,6 +338,8 @@ int route_pass(const moe_shape_t *s, const moe_weights_t *w, const void *x, int 
 
 }  // namespace
 
+int moe::api_fail(int code, const char *what) { return fail(code, what); }
+
 extern "C" {
 
 size_t moe_workspace_bytes(const moe_shape_t *shape)
