@@ -114,7 +114,13 @@ void launch_down_mxfp4(const ExpertArgs &a, hipStream_t st);
 // projection of every (t, j) pair and the weighted combine in one kernel,
 // writing y directly (the staging rows and the combine pass are skipped).
 bool down_combine_mxfp4_ok(const ExpertArgs &a);
-void launch_down_combine_mxfp4(const ExpertArgs &a, hipStream_t st);
+void launch_down_combine_mxfp4(const ExpertArgs &a, hipStream_t st);  // row_of null: pair order
+// Decode rows without the permutation: gate+up of every (t, j) pair taking
+// its expert from the router's logits (the same selection as the routing
+// kernels), h in pair order, and the indices and weights into topk_idx /
+// topk_w.  Followed by launch_down_combine_mxfp4 with row_of null.
+bool gate_up_mxfp4_pair_ok(const ExpertArgs &a);
+void launch_gate_up_mxfp4_pair(const ExpertArgs &a, const float *logits, hipStream_t st);
 // OCP row-major MXFP4 (codes [E, N, K/2], scales [E, N, K/32]) into the
 // packed layout the MXFP4 kernels read.
 void launch_pack_mxfp4(int E, int N, int K, const uint8_t *codes, const uint8_t *scales,

@@ -395,6 +395,54 @@ int moe_forward(const moe_shape_t *s, const moe_weights_t *w, const void *x, voi
         Layout Lw = L;
         Lw.max_tiles_gu = max_tiles(n, s, L.bm_gu);
         Lw.max_tiles_dc = max_tiles(n, s, L.bm_dc);
+        // Decode rows with MXFP4 experts: logits, then gate+up straight from
+        // them (the pairs in token order, no permutation), then down + combine.
+        {
+            moe::ExpertArgs d = expert_shape(s, n);
+            d.x = xc;
+            d.w_gate = w->w_gate;
+            d.w_up = w->w_up;
+            d.w_down = w->w_down;
+            d.s_gate = w->s_gate;
+            d.s_up = w->s_up;
+            d.s_down = w->s_down;
+            d.topk_idx = idx;
+            d.topk_w = wts;
+            d.h = wsb + Lw.h;
+            d.y = yc;
+            if (moe::gate_up_mxfp4_pair_ok(d)) {
+                moe::RouterArgs r{};
+                r.x = xc;
+                r.wr = w->router_w;
+                r.bias = w->router_bias;
+                r.logits = (float *)(wsb + Lw.logits);
+                r.T = n;
+                r.H = s->H;
+                r.E = s->E;
+                r.k = s->top_k;
+                r.act = moe::ACT_BF16;
+                {
+                    StageScope sc(0, st);
+                    moe::launch_router_small(r, st);
+                }
+                if ((rc = launched("router")))
+                    return rc;
+                {
+                    StageScope sc(2, st);
+                    moe::launch_gate_up_mxfp4_pair(d, r.logits, st);
+                }
+                if ((rc = launched("gate_up")))
+                    return rc;
+                d.row_of = nullptr;  // h rows in pair order
+                {
+                    StageScope sc(3, st);
+                    moe::launch_down_combine_mxfp4(d, st);
+                }
+                if ((rc = launched("down")))
+                    return rc;
+                continue;
+            }
+        }
         rc = route_pass(s, w, xc, n, idx, wts, wsb, Lw, st);
         if (rc)
             return rc;

@@ -34,6 +34,7 @@
 // applies to row (column) r and K block b.
 #include "common.h"
 #include "kernels.h"
+#include "topk.h"
 
 #include <algorithm>
 #include <cstdlib>
@@ -392,6 +393,107 @@ __global__ __launch_bounds__(64 * NW, WF ? 2 : 3) void expert_mxfp4(MxP p, const
     }
 }
 
+// Gate+up of decode rows (T <= 8) straight from the router's logits, with
+// no permutation pass: one workgroup per (token t, slot j) pair and 16 * NW
+// columns of both matrices.  Its waves read the token's logits and select
+// its top k with the same wave selection as the routing kernels (so the
+// same experts in the same order), take expert idx[t, j], quantise the
+// token's activation row into LDS (hi / lo MXFP8, as the grouped kernel
+// does) and stream their 16 columns' weights over the whole K.  The h row
+// of pair t * k + j is written in pair order; the workgroup of pair (t, 0)
+// and column block 0 also writes the token's indices and weights.  With
+// decode rows every expert has about one row (a 6-row verify block puts its
+// 48 pairs on ~47 experts), so grouping the pairs by expert first would
+// save almost no weight bytes and costs a launch.  WF: the weights are
+// requested right after the selection and the row is quantised while they
+// are in flight (two workgroups' registers per SIMD pair), else the row is
+// quantised first and three fit.
+struct MxPairP {
+    const uint16_t *x;            // [T, H]
+    const float *logits;          // [T, E]
+    const uint8_t *c0, *c1;       // gate / up codes, packed
+    const uint8_t *s0, *s1;       // their scales, packed
+    uint16_t *h;                  // [T * k, I]: the row of pair t * k + j
+    int32_t *idx;                 // [T, k]
+    float *w;                     // [T, k]
+    int T, H, E, k, I;
+};
+
+template <int NW, int NQ, int PER, bool WF>
+__global__ __launch_bounds__(64 * NW, WF ? 2 : 3) void expert_mxfp4_pair(MxPairP p)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int pr = blockIdx.y, t = pr / p.k, j = pr - t * p.k;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int K = p.H, nblk = K / 32, ld = K + MX_PAD;  // K = NQ * 128
+    uint8_t *ahi = smem, *alo = ahi + ld, *shi = alo + ld, *slo = shi + nblk;
+
+    // The token's logits and its activation row, requested together.
+    float v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+        v[i] = lane + 64 * i < p.E ? p.logits[(int64_t)t * p.E + lane + 64 * i] : 0.0f;
+    const uint16_t *xrow = p.x + (int64_t)t * p.H;
+    uint4 raw[4];
+    if (tid < nblk)
+        block_load(raw, xrow + tid * 32);
+    auto quantise = [&]() {
+        if (tid < nblk)
+            block_quantise(raw, 0, tid, K, ahi, alo, shi, slo);
+        for (int q = tid + 64 * NW; q < nblk; q += 64 * NW) {  // rows wider than the workgroup
+            uint4 r2[4];
+            block_load(r2, xrow + q * 32);
+            block_quantise(r2, 0, q, K, ahi, alo, shi, slo);
+        }
+    };
+    if (!WF)
+        quantise();
+
+    // The pair's expert: rank j of the token's selection (every wave selects).
+    int my_e;
+    uint32_t my_k;
+    wave_topk_select<PER>(v, p.E, p.k, my_e, my_k);
+    const int e = __builtin_amdgcn_readlane(my_e, j);
+
+    // This wave's 16 columns of the gate and up matrices of expert e.
+    const int64_t blk = (int64_t)e * (p.I / 16) + blockIdx.x * NW + wave;
+    MxSlice<NQ> w[2];
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+        slice_load<NQ>(w[0], p.c0 + blk * NQ * 1024 + 16 * lane, p.s0 + (blk * 64 + lane) * NQ, 0,
+                       s, s + 1);
+        slice_load<NQ>(w[1], p.c1 + blk * NQ * 1024 + 16 * lane, p.s1 + (blk * 64 + lane) * NQ, 0,
+                       s, s + 1);
+        __builtin_amdgcn_sched_barrier(0);  // keep the issue order
+    }
+    if (WF)
+        quantise();
+    if (j == 0 && blockIdx.x == 0 && wave == 0)
+        wave_topk_weights(my_e, my_k, p.k, p.idx + (int64_t)t * p.k, p.w + (int64_t)t * p.k,
+                          nullptr);
+    lds_barrier();
+
+    floatx4 acc[2][1];
+    acc[0][0] = floatx4{0, 0, 0, 0};
+    acc[1][0] = floatx4{0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+        uint4 b[2][1];
+        int sb[2][1];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            b[m][0] = w[m].q[s];
+            sb[m][0] = (int)(w[m].sc[s / 4] >> (8 * (s % 4)) & 0xFF);
+        }
+        mx_step<2, 1>(b, sb, ahi, alo, shi, slo, ld, nblk, s, 0, acc);
+    }
+    // Every row of C is the token's row (all lanes fed row 0), so every lane
+    // stores its element 0 - four lanes the same value to each column -
+    // and no lane condition can pull the MFMAs under a partial mask.
+    const int n = (blockIdx.x * NW + wave) * 16 + (lane & 15);
+    p.h[(int64_t)pr * p.I + n] = f2bf(silu(acc[0][0][0]) * acc[1][0][0]);
+}
+
 // Down projection and combine for decode rows, one workgroup per (16 CB
 // output columns, token t): wave j takes pair (t, j) - its expert's 16 CB
 // weight rows over the whole K, and its h row, quantised by the wave into its
@@ -420,7 +522,9 @@ __global__ __launch_bounds__(512) void expert_mxfp4_down_tok(MxTokP p)
     const int wst = (2 * ld + 2 * nblk + 15) & ~15;  // a wave's LDS area (16-byte aligned)
     const int pr = t * p.k + j;
     const int e = __builtin_amdgcn_readfirstlane(p.idx[pr]);
-    const int row = __builtin_amdgcn_readfirstlane(p.row_of[pr]);
+    // the h row of the pair: from the permutation, or the pair itself when
+    // gate+up wrote its rows in pair order
+    const int row = p.row_of ? __builtin_amdgcn_readfirstlane(p.row_of[pr]) : pr;
     uint8_t *ahi = smem + j * wst;
     uint8_t *alo = ahi + ld, *shi = alo + ld, *slo = shi + nblk;
     float *s_o = (float *)(smem + p.k * wst);  // [k][CB][64]
@@ -624,7 +728,7 @@ void launch_pack_mxfp4(int E, int N, int K, const uint8_t *codes, const uint8_t 
 bool down_combine_mxfp4_ok(const ExpertArgs &a)
 {
     return a.wdt == W_MXFP4 && a.act == ACT_BF16 && a.T >= 1 && a.T <= 8 && a.I_shared == 0 &&
-           a.k <= 8 && a.I % 128 == 0 && a.I <= 1024 && a.topk_idx && a.row_of && a.y;
+           a.k <= 8 && a.I % 128 == 0 && a.I <= 1024 && a.topk_idx && a.y;
 }
 
 constexpr int MX_DECODE_CUS = 256;  // compute units of an MI355X
@@ -670,6 +774,70 @@ void launch_down_combine_mxfp4(const ExpertArgs &a, hipStream_t st)
     case 6: down_tok<6>(p, a.T, st); break;
     case 7: down_tok<7>(p, a.T, st); break;
     default: down_tok<8>(p, a.T, st); break;
+    }
+}
+
+namespace {
+
+template <int NQ, int PER>
+void pair_launch(const MxPairP &p, hipStream_t st)
+{
+    const size_t lds = 2 * (size_t)(p.H + MX_PAD) + 2 * (size_t)(p.H / 32);
+    constexpr int NW = 2;
+    const dim3 grid(p.I / (16 * NW), p.T * p.k);
+    // a single row: weights first (the grid is far smaller than the chip)
+    if (p.T == 1)
+        expert_mxfp4_pair<NW, NQ, PER, true><<<grid, 64 * NW, lds, st>>>(p);
+    else
+        expert_mxfp4_pair<NW, NQ, PER, false><<<grid, 64 * NW, lds, st>>>(p);
+}
+
+template <int NQ>
+void pair_per(const MxPairP &p, hipStream_t st)
+{
+    switch (topk_per(p.E)) {
+    case 1: pair_launch<NQ, 1>(p, st); break;
+    case 2: pair_launch<NQ, 2>(p, st); break;
+    case 4: pair_launch<NQ, 4>(p, st); break;
+    case 8: pair_launch<NQ, 8>(p, st); break;
+    default: pair_launch<NQ, 16>(p, st); break;
+    }
+}
+
+}  // namespace
+
+bool gate_up_mxfp4_pair_ok(const ExpertArgs &a)
+{
+    const int q = a.H / 128;
+    return a.wdt == W_MXFP4 && a.act == ACT_BF16 && a.T >= 1 && a.T <= 8 && a.I_shared == 0 &&
+           a.k <= 8 && a.I % 128 == 0 && a.I <= 1024 && a.E <= 1023 && a.topk_idx &&
+           a.topk_w && a.y && (q == 1 || q == 2 || q == 4 || q == 6 || q == 8 || q == 16);
+}
+
+void launch_gate_up_mxfp4_pair(const ExpertArgs &a, const float *logits, hipStream_t st)
+{
+    MxPairP p;
+    p.x = (const uint16_t *)a.x;
+    p.logits = logits;
+    p.c0 = (const uint8_t *)a.w_gate;
+    p.c1 = (const uint8_t *)a.w_up;
+    p.s0 = a.s_gate;
+    p.s1 = a.s_up;
+    p.h = (uint16_t *)a.h;
+    p.idx = const_cast<int32_t *>(a.topk_idx);
+    p.w = const_cast<float *>(a.topk_w);
+    p.T = a.T;
+    p.H = a.H;
+    p.E = a.E;
+    p.k = a.k;
+    p.I = a.I;
+    switch (a.H / 128) {
+    case 1: pair_per<1>(p, st); break;
+    case 2: pair_per<2>(p, st); break;
+    case 4: pair_per<4>(p, st); break;
+    case 6: pair_per<6>(p, st); break;
+    case 8: pair_per<8>(p, st); break;
+    default: pair_per<16>(p, st); break;
     }
 }
 

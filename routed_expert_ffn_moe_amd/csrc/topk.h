@@ -49,18 +49,16 @@ __device__ __forceinline__ int wave_min_i32(int v)
     return __builtin_amdgcn_readlane(m, 63);
 }
 
-// Top-k of one token's router logits and their weights, computed by one
-// wave.  Lane l holds logits l, l+64, ... (E <= 64*PER) in val, sorted once into
-// descending order.  k rounds each take the best remaining (logit, expert)
-// pair of the wave, the head of one lane's list: larger logit first, equal
-// logits by lower expert index; NaN ranks as -inf.  So the pairs come out in
-// rank order, and the weights are the softmax over the selected logits (the
-// full softmax renormalised), summed in rank order.
-// Writes idx[0..k) and w[0..k) in rank order, and sidx[0..k) if given.
+// Top-k of one token's router logits, selected by one wave.  Lane l holds
+// logits l, l+64, ... (E <= 64*PER) in val, sorted once into descending
+// order.  k rounds each take the best remaining (logit, expert) pair of the
+// wave, the head of one lane's list: larger logit first, equal logits by
+// lower expert index; NaN ranks as -inf.  So the pairs come out in rank
+// order: lane r < k ends with the expert of rank r in my_e and its key in
+// my_k (the other lanes with 0).
 template <int PER>
-__device__ __forceinline__ void wave_topk_vals(const float (&val)[PER], int E, int k,
-                                               int32_t *__restrict__ idx, float *__restrict__ w,
-                                               int *sidx)
+__device__ __forceinline__ void wave_topk_select(const float (&val)[PER], int E, int k, int &my_e,
+                                                 uint32_t &my_k)
 {
     const int lane = threadIdx.x & 63;
     uint32_t key[PER];  // 0 for the slots past E: below every logit
@@ -84,8 +82,8 @@ __device__ __forceinline__ void wave_topk_vals(const float (&val)[PER], int E, i
                 slot[i] = slot[i + 1];
                 slot[i + 1] = ts;
             }
-    int my_e = 0;
-    uint32_t my_k = 0;
+    my_e = 0;
+    my_k = 0;
     for (int r = 0; r < k; ++r) {
         const uint32_t M = wave_max_u32(key[0]);
         const uint64_t tie = __ballot(key[0] == M);
@@ -110,7 +108,17 @@ __device__ __forceinline__ void wave_topk_vals(const float (&val)[PER], int E, i
             key[PER - 1] = 0u;
         }
     }
-    // softmax of the selected logits; the sum runs in rank order
+}
+
+// The weights of a selection (wave_topk_select's my_e, my_k): the softmax
+// over the selected logits (the full softmax renormalised over the
+// selection), summed in rank order.  Lanes r < k write idx[r], w[r] and, if
+// given, sidx[r].
+__device__ __forceinline__ void wave_topk_weights(int my_e, uint32_t my_k, int k,
+                                                  int32_t *__restrict__ idx,
+                                                  float *__restrict__ w, int *sidx)
+{
+    const int lane = threadIdx.x & 63;
     const float mx = key_value(__builtin_amdgcn_readlane(my_k, 0));
     const float ex = lane < k ? expf(key_value(my_k) - mx) : 0.0f;
     float z = 0.0f;
@@ -122,6 +130,19 @@ __device__ __forceinline__ void wave_topk_vals(const float (&val)[PER], int E, i
         if (sidx)
             sidx[lane] = my_e;
     }
+}
+
+// Top-k and weights: writes idx[0..k) and w[0..k) in rank order, and
+// sidx[0..k) if given.
+template <int PER>
+__device__ __forceinline__ void wave_topk_vals(const float (&val)[PER], int E, int k,
+                                               int32_t *__restrict__ idx, float *__restrict__ w,
+                                               int *sidx)
+{
+    int my_e;
+    uint32_t my_k;
+    wave_topk_select<PER>(val, E, k, my_e, my_k);
+    wave_topk_weights(my_e, my_k, k, idx, w, sidx);
 }
 
 // The same, reading the token's E logits from memory.
