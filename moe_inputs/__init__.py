@@ -52,6 +52,11 @@ CONFIGS: Dict[str, dict] = {
     "c4_t1": dict(T=1, H=2048, E=256, top_k=8, I=768, I_shared=0, act="bf16", w="mxfp4",
                   bias=None, layer="L4", seed=5,
                   desc="decode row, MXFP4 experts: T=1 H=2048 E=256 top-8 I=768"),
+    # the MXFP4 layer at a prefill chunk, skewed like the T=2048 bf16 chunk
+    "c4_p2048": dict(T=2048, H=2048, E=256, top_k=8, I=768, I_shared=0, act="bf16",
+                     w="mxfp4", bias="zipf1.1", layer="L4", seed=6,
+                     desc="prefill chunk, MXFP4 experts, Zipf(1.1) expert bias: "
+                          "T=2048 H=2048 E=256 top-8 I=768"),
 }
 LAYER_SEED = {"L0": 100, "L1": 101, "L3": 103, "L4": 104,
               # small layers of other shapes (the tests' sweep of kernel variants)

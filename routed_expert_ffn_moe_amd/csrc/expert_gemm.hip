@@ -411,33 +411,33 @@ void dispatch(const ExpertArgs &a, hipStream_t st)
 
 int gemm_bm_gu(const ExpertArgs &a)
 {
-    if (a.wdt == W_MXFP4)
-        return mxfp4_bm();
-    return stream_ok(a, true) ? stream_bm(a) : pick(a, true).bm;
+    if (stream_ok(a, true))
+        return stream_bm(a);
+    return a.wdt == W_MXFP4 ? mxfp4_bm() : pick(a, true).bm;
 }
 int gemm_bm_dc(const ExpertArgs &a)
 {
-    if (a.wdt == W_MXFP4)
-        return mxfp4_bm();
-    return stream_ok(a, false) ? stream_bm(a) : pick(a, false).bm;
+    if (stream_ok(a, false))
+        return stream_bm(a);
+    return a.wdt == W_MXFP4 ? mxfp4_bm() : pick(a, false).bm;
 }
 
 void launch_gate_up(const ExpertArgs &a, hipStream_t st)
 {
-    if (a.wdt == W_MXFP4)
-        launch_gate_up_mxfp4(a, st);
-    else if (stream_ok(a, true))
+    if (stream_ok(a, true))
         launch_stream(a, true, st);
+    else if (a.wdt == W_MXFP4)
+        launch_gate_up_mxfp4(a, st);
     else
         dispatch<true>(a, st);
 }
 
 void launch_down(const ExpertArgs &a, hipStream_t st)
 {
-    if (a.wdt == W_MXFP4)
-        launch_down_mxfp4(a, st);
-    else if (stream_ok(a, false))
+    if (stream_ok(a, false))
         launch_stream(a, false, st);
+    else if (a.wdt == W_MXFP4)
+        launch_down_mxfp4(a, st);
     else
         dispatch<false>(a, st);
 }

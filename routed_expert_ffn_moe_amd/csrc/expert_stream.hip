@@ -23,6 +23,20 @@
 //  * Work items are ordered expert-major (then weight tile, then row tile)
 //    and dealt out XCD by XCD in contiguous runs, so an expert's weight tiles
 //    and token rows are fetched into one XCD's L2 and reused there.
+//  * MXFP4 expert weights (W4, prefill chunks with more than 16 rows per
+//    expert on average): the same items and tiles, the weights streamed in
+//    the packed MXFP4 layout - one 16-byte load per lane and 16-row block
+//    covers 128 K (a lane holds 32 consecutive K of its row), plus the
+//    block's E8M0 scale byte - and turned into bf16 in registers with the
+//    scaled fp4 -> bf16 conversion (exact: an E2M1 value times a power of
+//    two has at most two significant bits).  The MFMA is the bf16 one with
+//    the K order permuted alike in both operands: in sub-step s of a 128-K
+//    chunk, lane group b holds K = 32b + 8s .. +7 of the weights and of the
+//    tokens.  Weight bytes are 17/32 of a byte per weight, so a slice streams
+//    in 0.27 of the bf16 time; the hi/lo MXFP8 split of the decode kernels
+//    would run the same number of MFMA passes with no gain in precision.
+//    Pages: "MoE prefill quantum", the section ruling out the hardware
+//    (dequantising MXFP4 and applying the scale streams at read speed).
 #include "common.h"
 #include "kernels.h"
 
@@ -43,8 +57,9 @@ constexpr int wrows_of(bool gu) { return gu ? 128 : 256; }
 
 struct StreamP {
     const uint16_t *x;        // GU: activations [T, H]; DC: h [rows, ldh]
-    const uint16_t *w0, *w1;  // routed matrices [E, N, K]
+    const uint16_t *w0, *w1;  // routed matrices [E, N, K] (MXFP4: packed codes)
     const uint16_t *s0, *s1;  // shared expert matrices [N, K]
+    const uint8_t *q0, *q1;   // MXFP4 only: packed E8M0 scales of w0, w1
     const int32_t *row_src, *offsets;
     const float *topk_w;
     uint16_t *out;            // GU: h; DC: stage
@@ -202,6 +217,94 @@ __device__ __forceinline__ void kchunk(bool full, const uint16_t *As, int slot0,
     }
 }
 
+// MXFP4 weights: 8 E2M1 codes (K = 8 consecutive elements, low nibble
+// first) times 2^(scale - 127) as a bf16 MFMA operand; the conversion takes
+// the E8M0 scale as the exponent field of an fp32.
+__device__ __forceinline__ bf16x8 fp4x8_bf16(uint32_t codes, uint32_t scale)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const float sc = __uint_as_float(scale << 23);
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Token fragments of sub-step s of a 128-wide staged chunk in the MXFP4
+// order: lane (l16, lg) holds token row mb*16 + l16, K = 32*lg + 8*s .. +7.
+template <int NMB, int SLD>
+__device__ __forceinline__ void frag_load_w4(bf16x8 (&tf)[NMB], const uint16_t *As, int s, int l16,
+                                             int lg, bool full)
+{
+#pragma unroll
+    for (int mb = 0; mb < NMB / 2; ++mb)
+        tf[mb] = as_bf16x8(*(const uint4 *)(As + (mb * 16 + l16) * SLD + lg * 32 + s * 8));
+    if (full || NMB < 2) {
+#pragma unroll
+        for (int mb = NMB / 2; mb < NMB; ++mb)
+            tf[mb] = as_bf16x8(*(const uint4 *)(As + (mb * 16 + l16) * SLD + lg * 32 + s * 8));
+    }
+}
+
+// One 128-wide K chunk with MXFP4 weights: ring slot `slot` holds this
+// chunk's codes and scales of every block and is refilled from chunk d = SD
+// ahead (codes at wl[m] + cb's block offset, scale bytes at sl[m]); the
+// token fragments of sub-step s + 1 are read from LDS before the MFMAs of
+// sub-step s.
+template <int MB, int NB, int CB, int SD, bool AGPR>
+__device__ __forceinline__ void kchunk_w4(bool full, const uint16_t *As, int slot, int l16, int lg,
+                                          uint4 (&bq)[SD][NB][CB], uint32_t (&sq)[SD][NB][CB],
+                                          const uint8_t *const (&wl)[NB],
+                                          const uint8_t *const (&sl)[NB], const int (&woff)[CB],
+                                          const int (&soff)[CB], floatx4 (&acc)[NB][CB][MB])
+{
+    constexpr int SLD = sld_of(128);
+    uint4 wq[NB][CB];
+    uint32_t ws[NB][CB];
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            wq[m][cb] = bq[slot][m][cb];
+            ws[m][cb] = sq[slot][m][cb];
+            bq[slot][m][cb] = wload<(MB <= 2)>((const uint16_t *)(wl[m] + woff[cb]));
+            sq[slot][m][cb] = sl[m][soff[cb]];
+        }
+    bf16x8 tf[2][MB];
+    frag_load_w4<MB, SLD>(tf[0], As, 0, l16, lg, full);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        if (st + 1 < 4)
+            frag_load_w4<MB, SLD>(tf[(st + 1) & 1], As, st + 1, l16, lg, full);
+        bf16x8 wf[NB][CB];
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const uint32_t c4[4] = {wq[m][cb].x, wq[m][cb].y, wq[m][cb].z, wq[m][cb].w};
+                wf[m][cb] = fp4x8_bf16(c4[st], ws[m][cb]);
+            }
+#pragma unroll
+        for (int mb = 0; mb < MB / 2; ++mb)
+#pragma unroll
+            for (int m = 0; m < NB; ++m)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+                    mac<AGPR>(acc[m][cb][mb], wf[m][cb], tf[st & 1][mb]);
+        if (full || MB < 2) {
+#pragma unroll
+            for (int mb = MB / 2; mb < MB; ++mb)
+#pragma unroll
+                for (int m = 0; m < NB; ++m)
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+                        mac<AGPR>(acc[m][cb][mb], wf[m][cb], tf[st & 1][mb]);
+        }
+    }
+}
+
 // Persistent: the workgroup walks its run of work items; the weight prefetch
 // ring and the token-chunk pipeline run on across item boundaries, so the
 // next item's first weights and rows are in flight while the current one
@@ -212,7 +315,7 @@ __device__ __forceinline__ void kchunk(bool full, const uint16_t *As, int slot0,
 // the LDS and L2 latency that one wave's own schedule cannot.
 constexpr int wg_per_cu(int bm) { return bm <= 16 ? 3 : bm <= 64 ? 2 : 1; }
 
-template <int BM, bool GU, int SD, int SKC>
+template <int BM, bool GU, int SD, int SKC, bool W4, int TL>
 __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
                                                                     const int4 *__restrict__ items)
 {
@@ -221,8 +324,9 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
     constexpr int CB = GU ? 2 : 4;             // 16-row weight blocks per wave and matrix
     constexpr int MB = BM / 16;                // 16-row token blocks
     constexpr int ACH = BM * (SKC / 8) / 256;  // 16-byte token chunks per thread
-    static_assert(SD == 4 || SD == 8, "prefetch ring depth in K steps");
-    static_assert((2 * SPC) % SD == 0, "ring slots line up with chunk pairs");
+    static_assert(W4 || SD == 4 || SD == 8, "prefetch ring depth in K steps");
+    static_assert(W4 || (2 * SPC) % SD == 0, "ring slots line up with chunk pairs");
+    static_assert(!W4 || (SD == 2 && SKC == 128), "MXFP4: a ring of two 128-K chunks");
     static_assert(ACH >= 1 && ACH * 256 == BM * SKC / 8, "token staging");
     static_assert(CB % 2 == 0 && 4 * CB * 16 == wrows_of(GU), "column blocks go in pairs");
     // the 128-row tiles' accumulators fill the accumulation registers
@@ -256,15 +360,32 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
     // holds 8 consecutive output columns per pair of blocks and stores them
     // as one 16-byte word.  One K step of a block is a contiguous kilobyte
     // (1024 elements per 32 K: offsets below scale K positions by 32).
-    int woff[CB];
+    // MXFP4: block cb of the wave is 16-row block n0/16 + wave*CB + cb of
+    // the expert (row 16 * block + l16), codes [blocks][Q][64 lanes][16 B]
+    // and scales [blocks][64 lanes][Q], Q = K / 128 chunks.
+    const int Q4 = K / 128;
+    int woff[CB], soff[CB];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-        woff[cb] = ((wave * CB / 2 + cb / 2) * (K / 32) * 2 + (cb & 1)) * 512 + lane * 8;
+    for (int cb = 0; cb < CB; ++cb) {
+        if (W4) {
+            woff[cb] = (wave * CB + cb) * Q4 * 1024 + lane * 16;  // bytes
+            soff[cb] = ((wave * CB + cb) * 64 + lane) * Q4;
+        } else {
+            woff[cb] = ((wave * CB / 2 + cb / 2) * (K / 32) * 2 + (cb & 1)) * 512 + lane * 8;
+            soff[cb] = 0;
+        }
+    }
     auto wbase = [&](const Item &it, int m) -> const uint16_t * {
+        if (W4)  // packed codes of the item's first block (bytes)
+            return (const uint16_t *)((const uint8_t *)(m == 0 ? p.w0 : p.w1) +
+                                      ((int64_t)it.g * (N / 16) + it.n0 / 16) * Q4 * 1024);
         const bool routed = it.g < p.E;
         const uint16_t *W = m == 0 ? (routed ? p.w0 + (int64_t)it.g * wstride : p.s0)
                                    : (routed ? p.w1 + (int64_t)it.g * wstride : p.s1);
         return W + (int64_t)it.n0 * K;
+    };
+    auto qbase = [&](const Item &it, int m) -> const uint8_t * {  // MXFP4 scales
+        return (m == 0 ? p.q0 : p.q1) + ((int64_t)it.g * (N / 16) + it.n0 / 16) * 64 * Q4;
     };
     int aoff[ACH];
 #pragma unroll
@@ -278,20 +399,32 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
 #pragma unroll
     for (int m = 0; m < NB; ++m)
         wc[m] = wbase(cur, m);
+    const uint8_t *qc[NB];
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+        qc[m] = W4 ? qbase(cur, m) : nullptr;
     uint4 bq[SD][NB][CB];
+    uint32_t sq[SD][NB][CB];
 #pragma unroll
     for (int d = 0; d < SD; ++d)
 #pragma unroll
         for (int m = 0; m < NB; ++m)
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-                bq[d][m][cb] = wload<(MB <= 2)>(wc[m] + woff[cb] + d * 1024);  // SD <= 8 <= K/32
+            for (int cb = 0; cb < CB; ++cb) {
+                if (W4) {  // chunk d (SD = 2 <= K / 128)
+                    bq[d][m][cb] = wload<(MB <= 2)>(
+                        (const uint16_t *)((const uint8_t *)wc[m] + woff[cb] + d * 1024));
+                    sq[d][m][cb] = qc[m][soff[cb] + d];
+                } else {
+                    bq[d][m][cb] = wload<(MB <= 2)>(wc[m] + woff[cb] + d * 1024);  // SD <= 8 <= K/32
+                    sq[d][m][cb] = 0;
+                }
+            }
     int aro[ACH], aro_n[ACH];
     item_rows<ACH, GU, SKC>(p, cur, tid, aro);
     item_rows<ACH, GU, SKC>(p, nxt, tid, aro_n);
-    // Token chunks in flight: TL ahead of the one in LDS (two measured no
-    // faster than one: the weights, not the token rows, set the pace).
-    constexpr int TL = 1;
+    // Token chunks in flight: TL (1 or 2) ahead of the one in LDS.
+    static_assert(TL == 1 || TL == 2, "token chunks in flight");
     u32v<ACH> rt[TL];
     rows_load<ACH>(rt[0], p.x, aro, (tid % RW) * 8);
     chunk_store<ACH>(rt[0], sA[0], aoff);
@@ -307,9 +440,12 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
         // Next item's weights; the last item points them at itself, so the
         // prefetches that run past it stay in bounds and no branch is needed.
         const uint16_t *wn[NB];
+        const uint8_t *qn[NB];
 #pragma unroll
-        for (int m = 0; m < NB; ++m)
+        for (int m = 0; m < NB; ++m) {
             wn[m] = j + 1 < nitems ? wbase(nxt, m) : wc[m];
+            qn[m] = W4 ? (j + 1 < nitems ? qbase(nxt, m) : qc[m]) : nullptr;
+        }
 
         floatx4 acc[NB][CB][MB];
 #pragma unroll
@@ -326,22 +462,37 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
             for (int h = 0; h < 2; ++h) {
                 const int cc = c + h;
                 const uint16_t *As = sA[buf];
-                // Weight chunks d = 0, 1, 2 after this one, from this item or
-                // (past its end) from the next one; branch-free on purpose.
-                const uint16_t *wl[3][NB];
-#pragma unroll
-                for (int d = 0; d < 3; ++d) {
-                    const int t = cc + d;
+                if (W4) {
+                    // the chunk SD = 2 ahead refills this one's ring slot
+                    const int t = cc + 2;
                     const int over = t >= nchunks;
-                    const int tk = (t - over * nchunks) * SKC * 32;  // packed: 32 per K
+                    const int tq = t - over * nchunks;
+                    const uint8_t *wl4[NB], *sl4[NB];
 #pragma unroll
-                    for (int m = 0; m < NB; ++m)
-                        wl[d][m] = (over ? wn[m] : wc[m]) + tk;
+                    for (int m = 0; m < NB; ++m) {
+                        wl4[m] = (const uint8_t *)(over ? wn[m] : wc[m]) + tq * 1024;
+                        sl4[m] = (over ? qn[m] : qc[m]) + tq;
+                    }
+                    kchunk_w4<MB, NB, CB, SD, AGPR>(full, As, h, l16, lg, bq, sq, wl4, sl4, woff,
+                                                    soff, acc);
+                } else {
+                    // Weight chunks d = 0, 1, 2 after this one, from this item
+                    // or (past its end) from the next one; branch-free on purpose.
+                    const uint16_t *wl[3][NB];
+#pragma unroll
+                    for (int d = 0; d < 3; ++d) {
+                        const int t = cc + d;
+                        const int over = t >= nchunks;
+                        const int tk = (t - over * nchunks) * SKC * 32;  // packed: 32 per K
+#pragma unroll
+                        for (int m = 0; m < NB; ++m)
+                            wl[d][m] = (over ? wn[m] : wc[m]) + tk;
+                    }
+                    // Items whose rows fit the first half of the row tile skip
+                    // the MFMAs of the second half (the tile's other empty row
+                    // blocks are computed: finer splits cost more than they save).
+                    kchunk<MB, NB, CB, SD, SKC, AGPR>(full, As, h * SPC, l16, lg, bq, wl, woff, acc);
                 }
-                // Items whose rows fit the first half of the row tile skip
-                // the MFMAs of the second half (the tile's other empty row
-                // blocks are computed: finer splits cost more than they save).
-                kchunk<MB, NB, CB, SD, SKC, AGPR>(full, As, h * SPC, l16, lg, bq, wl, woff, acc);
                 // Token chunk pipeline: rt[h % TL] holds the chunk after this
                 // one and is reloaded with the chunk TL + 1 ahead.
                 u32v<ACH> &ra = rt[h % TL];
@@ -364,15 +515,31 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
         if (AGPR)
             mfma_acc_drain();
         // Epilogue: for block pair q the lane holds columns n + 32q .. +7 of
-        // token row mb*16 + l16 (block 2q covers the first four).
+        // token row mb*16 + l16 (block 2q covers the first four); with MXFP4
+        // weights block cb gives columns n4 + 16 cb .. +3.
         const int n = cur.n0 + wave * 16 * CB + lg * 8;
+        const int n4 = cur.n0 + wave * 16 * CB + lg * 4;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int mr = mb * 16 + l16;
             if (mr >= cur.nrows)
                 continue;
             const int pos = cur.row0 + mr;
-            if (GU) {
+            if (W4) {
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    const floatx4 g = acc[0][cb][mb], u = acc[NB - 1][cb][mb];
+                    uint2 o;
+                    if (GU) {
+                        o.x = pack_bf2(silu(g[0]) * u[0], silu(g[1]) * u[1]);
+                        o.y = pack_bf2(silu(g[2]) * u[2], silu(g[3]) * u[3]);
+                    } else {
+                        o.x = pack_bf2(g[0], g[1]);
+                        o.y = pack_bf2(g[2], g[3]);
+                    }
+                    *(uint2 *)(p.out + (int64_t)pos * (GU ? p.ldh : p.H) + n4 + 16 * cb) = o;
+                }
+            } else if (GU) {
 #pragma unroll
                 for (int q = 0; q < CB / 2; ++q) {
                     const floatx4 g0 = acc[0][2 * q][mb], u0 = acc[NB - 1][2 * q][mb];
@@ -400,8 +567,10 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
         cur = nxt;
         nxt = nn;
 #pragma unroll
-        for (int m = 0; m < NB; ++m)
+        for (int m = 0; m < NB; ++m) {
             wc[m] = wn[m];
+            qc[m] = qn[m];
+        }
 #pragma unroll
         for (int i = 0; i < ACH; ++i)
             aro[i] = aro_n[i];
@@ -409,13 +578,15 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
     }
 }
 
-template <int BM, bool GU, int SD, int SKC>
+template <int BM, bool GU, int SD, int SKC, bool W4, int TL>
 void run(const ExpertArgs &a, hipStream_t st)
 {
     StreamP p;
     p.x = (const uint16_t *)(GU ? a.x : a.h);
     p.w0 = (const uint16_t *)(GU ? a.w_gate : a.w_down);
     p.w1 = (const uint16_t *)(GU ? a.w_up : nullptr);
+    p.q0 = W4 ? (GU ? a.s_gate : a.s_down) : nullptr;
+    p.q1 = W4 && GU ? a.s_up : nullptr;
     p.s0 = (const uint16_t *)(GU ? a.sh_gate : a.sh_down);
     p.s1 = (const uint16_t *)(GU ? a.sh_up : nullptr);
     p.row_src = a.row_src;
@@ -451,7 +622,7 @@ void run(const ExpertArgs &a, hipStream_t st)
     int &occ = per_cu[GU ? 1 : 0];
     if (!occ) {
         int b = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, expert_stream<BM, GU, SD, SKC>, 256,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, expert_stream<BM, GU, SD, SKC, W4, TL>, 256,
                                                          0) != hipSuccess ||
             b < 1)
             b = 1;
@@ -459,14 +630,22 @@ void run(const ExpertArgs &a, hipStream_t st)
     }
     const int64_t per_xcd = (items + 7) / 8;
     const int64_t slots = std::min<int64_t>(per_xcd, (int64_t)(cus / 8) * occ);
-    expert_stream<BM, GU, SD, SKC><<<(unsigned)(slots * 8), 256, 0, st>>>(p, p.items);
+    expert_stream<BM, GU, SD, SKC, W4, TL><<<(unsigned)(slots * 8), 256, 0, st>>>(p, p.items);
 }
 
 }  // namespace
 
+// MXFP4 experts take the streaming kernels in prefill passes (more than 16
+// rows per expert on average); decode and verify passes take the fp4-MFMA
+// kernels of mxfp4.hip.
+static bool stream_w4(const ExpertArgs &a)
+{
+    return a.wdt == W_MXFP4 && a.I_shared == 0 && (int64_t)a.shape_T * a.k > 16 * (int64_t)a.E;
+}
+
 bool stream_ok(const ExpertArgs &a, bool gu)
 {
-    if (a.act != ACT_BF16 || a.wdt != W_BF16)
+    if (a.act != ACT_BF16 || !(a.wdt == W_BF16 || stream_w4(a)))
         return false;
     // one width for every item of a launch: no shared expert, or one as wide
     // as the routed experts
@@ -538,19 +717,37 @@ static int stream_skc(int K, int bm)
     return K % 512 == 0 && bm <= 32 ? 256 : 128;
 }
 
+// Token chunks in flight for the MXFP4 kernels (their fp4 weight ring frees
+// the registers of a second one); MOE_STREAM_TL (1 or 2) overrides it for
+// tuning runs.
+static int stream_tl_w4()
+{
+    static const int forced = [] {
+        const char *e = getenv("MOE_STREAM_TL");
+        const int v = e ? atoi(e) : 0;
+        return (v == 1 || v == 2) ? v : 0;
+    }();
+    return forced ? forced : 2;
+}
+
 template <int BM, bool GU, int SKC>
 static void run_skc(const ExpertArgs &a, hipStream_t st)
 {
     if (stream_sd(BM) == 8)
-        run<BM, GU, 8, SKC>(a, st);
+        run<BM, GU, 8, SKC, false, 1>(a, st);
     else
-        run<BM, GU, 4, SKC>(a, st);
+        run<BM, GU, 4, SKC, false, 1>(a, st);
 }
 
 template <int BM, bool GU>
 static void run_sd(const ExpertArgs &a, hipStream_t st)
 {
-    if (stream_skc(GU ? a.H : a.I, BM) == 256)
+    if (a.wdt == W_MXFP4) {  // a ring of two 128-K chunks of fp4 codes
+        if (stream_tl_w4() == 1)
+            run<BM, GU, 2, 128, true, 1>(a, st);
+        else
+            run<BM, GU, 2, 128, true, 2>(a, st);
+    } else if (stream_skc(GU ? a.H : a.I, BM) == 256)
         run_skc<BM, GU, 256>(a, st);
     else
         run_skc<BM, GU, 128>(a, st);

@@ -329,6 +329,57 @@ def test_mxfp4_path_matches_bf16_path_on_the_same_weights(T, hot):
     check_err("bf16 on dequantised weights vs oracle T=%d" % T, hx.rel_err(y16h, y_ref), "bf16")
 
 
+@pytest.mark.parametrize("T,bias", [(600, None), (1024, None), (2048, "zipf1.1"),
+                                    (4096, None)])
+def test_mxfp4_prefill_chunks(T, bias):
+    """MXFP4 experts in prefill chunks (more than 16 rows per expert on
+    average): the streaming kernels with fp4 weights converted to bf16 in
+    registers, row tiles of 32 (T=600, 1024) and 128 (T=2048 skewed, 4096),
+    routing on every token and y on tile-edge rows of the most-loaded
+    experts (all rows at T=600)."""
+    say("[mxfp4 prefill] T =", T, bias)
+    c, g = layer("c4_t6")
+    c = dict(c, T=T, seed=8000 + T, bias=bias)
+    lay = g.lay
+    gl = g
+    if bias is not None:
+        lay = mi.LayerData(c=c, router_w=g.lay.router_w, router_bias=mi.router_bias(c),
+                           w_gate=g.lay.w_gate, w_up=g.lay.w_up, w_down=g.lay.w_down,
+                           s_gate=g.lay.s_gate, s_up=g.lay.s_up, s_down=g.lay.s_down)
+        gl = hx.GpuLayer(c, lay)
+    x = hx.margin_x(c, lay)
+    y, idx, w = gl.forward(hx.act_torch(x, c["act"], "cuda"))
+    idx_r, w_r, _ = oracle.route(hx.router_only_layer(c, lay), x)
+    assert np.array_equal(idx.cpu().numpy(), idx_r)
+    assert np.abs(w.cpu().numpy() - w_r).max() <= hx.W_TOL
+    tokens = None if T <= 600 else tile_edge_tokens(idx_r, c["E"], c["top_k"], 0,
+                                                    bm=32 if T <= 1024 else 128)
+    experts = sorted(set((idx_r if tokens is None else idx_r[tokens]).reshape(-1).tolist()))
+    y_ref, _, _ = oracle.forward(hx.oracle_layer(c, lay, experts), x, tokens)
+    yh = hx.y_host(y, c["act"])
+    check_err("mxfp4 prefill T=%d%s (%s rows)" % (T, " zipf" if bias else "",
+                                                 "all" if tokens is None else tokens.size),
+              hx.rel_err(yh if tokens is None else yh[tokens], y_ref), "mxfp4")
+
+
+def test_mxfp4_prefill_matches_bf16_on_the_same_weights():
+    """The MXFP4 streaming kernels against the bf16 streaming kernels run on
+    the dequantised weights (K summed in another order), bf16 tolerance."""
+    T = 1024
+    c, g = layer("c4_t6")
+    c = dict(c, T=T, seed=8500)
+    x = hx.margin_x(c, g.lay)
+    idx_r, _, _ = oracle.route(hx.router_only_layer(c, g.lay), x)
+    experts = sorted(set(idx_r.reshape(-1).tolist()))
+    xd = hx.act_torch(x, c["act"], "cuda")
+    y4, i4, w4 = hx.GpuLayer(c, g.lay).forward(xd)
+    y16, i16, w16 = hx.GpuLayer(dict(c, w="bf16"),
+                                _dequantised_bf16_layer(c, g.lay, experts)).forward(xd)
+    assert torch.equal(i4, i16) and torch.equal(w4, w16)
+    check_err("mxfp4 vs bf16 stream kernels, same weights, T=%d" % T,
+              hx.rel_err(hx.y_host(y4, "bf16"), hx.y_host(y16, "bf16")), "bf16")
+
+
 @pytest.mark.parametrize("T", [5, 100])
 def test_shared_expert_short_passes(T):
     """The shared expert (group E, every token) through the short-pass
@@ -421,6 +472,70 @@ def test_graph_replay_matches_eager(name):
         y_e, i_e, w_e = g.forward(xs[r])
         assert torch.equal(idx, i_e) and torch.equal(w, w_e)
         assert torch.equal(y, y_e)
+
+
+@pytest.mark.parametrize("name,L", [("c4_t1", 4), ("c4_t6", 3)])
+def test_decode_stack_in_one_graph(name, L):
+    """L decode layers (MXFP4 experts, each its own weights) chained, the
+    output of one the input of the next, captured into one HIP graph: each
+    replay on new inputs equals the eager chain bit for bit, and every layer
+    of the chain matches the oracle run on that layer's own input (routing
+    bit-exact where the oracle's top-k margin exceeds fp32 logit rounding,
+    y within the MXFP4 bar)."""
+    say("[stack] config", name, "layers", L)
+    c = mi.cfg(name)
+    T = c["T"]
+    lays = [mi.make_layer(c, "cuda", 10 + l) for l in range(L)]
+    gls = [hx.GpuLayer(c, lay) for lay in lays]
+    shape = gls[0].shape(T)
+    ws = torch.empty(max(moe.moe_workspace_bytes(shape), 256), dtype=torch.uint8, device="cuda")
+    bufs = [torch.empty((T, c["H"]), dtype=torch.bfloat16, device="cuda") for _ in range(L + 1)]
+    idx = torch.empty((L, T, c["top_k"]), dtype=torch.int32, device="cuda")
+    w = torch.empty((L, T, c["top_k"]), dtype=torch.float32, device="cuda")
+
+    def stack():
+        for l in range(L):
+            moe.moe_forward(shape, gls[l].weights, bufs[l], bufs[l + 1], idx[l], w[l], ws)
+
+    xs = [hx.act_torch(hx.margin_x(dict(c, seed=c["seed"] + 900 + r), lays[0]), "bf16", "cuda")
+          for r in range(2)]
+    s = torch.cuda.Stream()
+    bufs[0].copy_(xs[0])
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        stack()
+        s.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            stack()
+    torch.cuda.synchronize()
+    for r in (1, 0):
+        bufs[0].copy_(xs[r])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        g_out = [b.clone() for b in bufs]
+        g_idx, g_w = idx.clone(), w.clone()
+        stack()
+        torch.cuda.synchronize()
+        for l in range(L):
+            assert torch.equal(g_out[l + 1], bufs[l + 1]), ("graph vs eager", r, l)
+        assert torch.equal(g_idx, idx) and torch.equal(g_w, w)
+        for l in range(L):
+            xin = hx.y_host(bufs[l], "bf16").astype(np.float32)
+            xh = mi.bf16_bits(xin)  # exactly the layer's bf16 input
+            Lr = hx.router_only_layer(c, lays[l])
+            idx_r, _, _ = oracle.route(Lr, xh)
+            gap = oracle.topk_margin(Lr, xh)
+            sure = gap > 1e-5  # far above fp32 rounding of the logits
+            assert np.array_equal(idx[l].cpu().numpy()[sure], idx_r[sure]), ("routing", r, l)
+            experts = sorted(set(idx_r.reshape(-1).tolist()) |
+                             set(idx[l].cpu().numpy().reshape(-1).tolist()))
+            y_ref, _, _ = oracle.forward(hx.oracle_layer(c, lays[l], experts), xh)
+            yg = hx.y_host(bufs[l + 1], "bf16")
+            if sure.all():
+                check_err("stack %s layer %d replay %d" % (name, l, r), hx.rel_err(yg, y_ref),
+                          "mxfp4")
 
 
 def test_pack_mxfp4_layout():
