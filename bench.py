@@ -390,6 +390,58 @@ def describe(wl, wall, stages, steps, graph_wall=None):
     return out
 
 
+def decode_stack(name, L, steps, warmup):
+    """L MoE layers of the decode workload `name` chained as a model's MoE
+    layers run, the output of layer l the input of layer l + 1, each layer
+    with its own weights: per-layer time with the L calls launched one after
+    the other (eager) and with all of them captured into one HIP graph and
+    replayed as one submission."""
+    import torch
+
+    import moe_inputs as mi
+    import routed_expert_ffn_moe_amd as moe
+    wl = Workload(name, wsets=L)
+    c = wl.c
+    bufs = [wl.x] + [torch.empty_like(wl.x) for _ in range(L)]
+    idx = torch.empty((L, c["T"], c["top_k"]), dtype=torch.int32, device="cuda")
+    w = torch.empty((L, c["T"], c["top_k"]), dtype=torch.float32, device="cuda")
+
+    def stack():
+        for l in range(L):
+            moe.moe_forward(wl.shape, wl.weights[l], bufs[l], bufs[l + 1], idx[l], w[l], wl.ws)
+
+    for _ in range(warmup):
+        stack()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        stack()
+    torch.cuda.synchronize()
+    eager = (time.perf_counter() - t0) / steps
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        stack()
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            stack()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph = (time.perf_counter() - t0) / steps
+    del wl, bufs
+    torch.cuda.empty_cache()
+    return {"workload": mi.cfg(name)["desc"], "layers": L,
+            "eager_us_per_layer": round(eager / L * 1e6, 2),
+            "graph_us_per_layer": round(graph / L * 1e6, 2),
+            "graph_tokens_per_s_per_layer": round(c["T"] / (graph / L), 1)}
+
+
 SWEEP_T = (128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768)
 
 
@@ -447,12 +499,14 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2")
-    ap.add_argument("--extra", default="c1,c3,c4_t6,c4_t1",
+    ap.add_argument("--extra", default="c1,c3,c4_t6,c4_t1,c4_p2048",
                     help="comma-separated secondary workloads ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the chunk-size sweep")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the ceiling probes")
+    ap.add_argument("--stack", type=int, default=16, metavar="L",
+                    help="layers of the decode stack timed eager and as one HIP graph (0: skip)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (calibrates HBM "
                          "byte counters) and exit")
@@ -525,6 +579,8 @@ def main():
         del w2
         torch.cuda.empty_cache()
     out["also"] = also
+    if args.stack:
+        out["decode_stack"] = [decode_stack(n, args.stack, 50, 5) for n in ("c4_t1", "c4_t6")]
     if not args.no_sweep:
         out["sweep"] = sweep(args.steps, args.warmup)
     if not args.no_cpu_baseline:
