@@ -442,6 +442,43 @@ def decode_stack(name, L, steps, warmup):
             "graph_tokens_per_s_per_layer": round(c["T"] / (graph / L), 1)}
 
 
+SMALL_T = (1, 2, 4, 6, 8, 16, 32, 64)
+
+
+def small_t_sweep(steps, warmup, Ts=SMALL_T):
+    """The MXFP4 decode/verify layer (H=2048, 256 experts top-8, I=768) at
+    small T: per-step time, gate+up stage time and its fraction of 8 TB/s,
+    weight sets rotated so the weights come from HBM."""
+    import moe_inputs as mi
+    torch = __import__("torch")
+    c0 = mi.cfg("c4_t6")
+    wl = Workload("c4_t6", wsets=16, cfg=dict(c0, T=max(Ts)))
+    x_all = wl.x
+    out = []
+    for T in Ts:
+        wl.c = dict(c0, T=T)
+        wl.x = x_all[:T]
+        wl.shape = wl.moe.make_shape(T, c0["H"], c0["E"], c0["top_k"], c0["I"], 0, 0,
+                                     c0["act"], c0["w"])
+        nb = wl.moe.moe_workspace_bytes(wl.shape)
+        if wl.ws.numel() < nb:
+            wl.ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        wl.y = torch.empty_like(wl.x)
+        wl.idx = torch.empty((T, c0["top_k"]), dtype=torch.int32, device="cuda")
+        wl.w = torch.empty((T, c0["top_k"]), dtype=torch.float32, device="cuda")
+        n = max(steps, 200)
+        wall, stages = wl.time(n, warmup)
+        d = describe(wl, wall, stages, n)
+        out.append({"T": T, "us_per_step": d["us_per_step"], "tokens_per_s": d["tokens_per_s"],
+                    "experts_touched": d["experts_touched"],
+                    "gate_up_us": d["stages_us"]["gate_up"],
+                    "gate_up_frac_hbm": d["grouped_gemms"]["gate_up"]["frac_hbm"],
+                    "layer_frac": d["layer"]["frac"]})
+    del wl
+    torch.cuda.empty_cache()
+    return {"layer": "H=2048 E=256 top-8 I=768, MXFP4 experts, 16 weight sets", "points": out}
+
+
 SWEEP_T = (128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768)
 
 
@@ -504,6 +541,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the chunk-size sweep")
+    ap.add_argument("--no-small-sweep", action="store_true",
+                    help="skip the small-T sweep of the MXFP4 layer")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the ceiling probes")
     ap.add_argument("--stack", type=int, default=16, metavar="L",
                     help="layers of the decode stack timed eager and as one HIP graph (0: skip)")
@@ -581,6 +620,8 @@ def main():
     out["also"] = also
     if args.stack:
         out["decode_stack"] = [decode_stack(n, args.stack, 50, 5) for n in ("c4_t1", "c4_t6")]
+    if not args.no_small_sweep:
+        out["small_T_mxfp4"] = small_t_sweep(args.steps, args.warmup)
     if not args.no_sweep:
         out["sweep"] = sweep(args.steps, args.warmup)
     if not args.no_cpu_baseline:

@@ -21,6 +21,11 @@ struct RouterArgs {
     int32_t *idx;         // [T, k]
     float *w;             // [T, k]
     int32_t *ticket;      // route_small's counter, cleared by router_small (or null)
+    // With xq set, router_small also writes every token row as an MXFP8
+    // hi / lo record of mx_row_bytes(H) bytes (mxfp8.h) at xq + t * that,
+    // for the MXFP4 kernels; xq is ignored by the other routers, which
+    // leave the expert kernels to quantise their rows themselves.
+    uint8_t *xq;
     // With hist set, the segmented router also counts the pairs of each
     // permutation block per expert into hist [nblk, E] (cleared first).
     int32_t *hist;
@@ -65,6 +70,10 @@ void launch_permute(const PermuteArgs &a, hipStream_t st);
 // permutation in two launches.
 bool route_small_ok(int T, int k, int E, int H, int act);
 int router_small_rw(int E, int H, int act);  // waves of router_small, 0 if it does not apply
+// router_small can write the MXFP8 row records (RouterArgs::xq) for this
+// shape, and the bytes they take for T tokens.
+bool router_xq_ok(int E, int H, int act);
+size_t router_xq_bytes(int T, int H);
 void launch_router_small(const RouterArgs &r, hipStream_t st);  // logits only
 void launch_route_small(const RouterArgs &r, const PermuteArgs &a, hipStream_t st);  // top-k + permutation
 
@@ -73,6 +82,7 @@ void launch_route_small(const RouterArgs &r, const PermuteArgs &a, hipStream_t s
 // stage[row] = h[row] Wd^T, one staging row per grouped row.
 struct ExpertArgs {
     const void *x;                           // [T, H] act
+    const uint8_t *xq;                       // x as MXFP8 row records (router_small), or null
     const void *w_gate, *w_up, *w_down;      // routed weights (codes for MXFP4)
     const uint8_t *s_gate, *s_up, *s_down;   // MXFP4 scales
     const void *sh_gate, *sh_up, *sh_down;   // shared expert (act dtype)

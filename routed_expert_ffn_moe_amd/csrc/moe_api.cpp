@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -134,7 +135,8 @@ int check_weights(const moe_shape_t *s, const moe_weights_t *w)
 // Workspace layout of one pass of Tc tokens.
 struct Layout {
     size_t logits, wts, blk, counts, offsets, row_src, row_tok, row_of, tiles_gu, ntiles, tiles_dc,
-        items_gu, items_dc, h, stage, total;
+        items_gu, items_dc, h, stage, xq, total;
+    bool has_xq;  // MXFP4 passes routed by router_small: x quantised once per token
     int max_tiles_gu, max_tiles_dc, bm_gu, bm_dc, ntn_gu, ntn_dc;
 };
 
@@ -199,6 +201,19 @@ Layout layout(const moe_shape_t *s, int Tc)
     L.items_dc = take((size_t)L.max_tiles_dc * L.ntn_dc * 16);
     L.h = take((size_t)rows * ldh * esz);
     L.stage = take((size_t)rows * s->H * esz);
+    // decode, verify and other short passes with MXFP4 experts
+    const int act = s->act_dtype == MOE_BF16 ? moe::ACT_BF16 : moe::ACT_F32;
+    // The router quantising x once for all expert kernels is off unless
+    // MOE_MX_XQ=1 (read at every call, so workspace sizing and calls agree
+    // while it is unchanged): measured slower than each expert workgroup
+    // quantising its own rows (the router's extra work lies on the decode
+    // step's critical path, and copying a quantised row costs what
+    // quantising it does).  The results are bit-identical either way.
+    const char *xq_env = std::getenv("MOE_MX_XQ");
+    const bool xq_on = xq_env && xq_env[0] == '1';
+    L.has_xq = xq_on && s->w_dtype == MOE_MXFP4 && moe::router_xq_ok(s->E, s->H, act) &&
+               moe::route_small_ok(Tc, s->top_k, s->E, s->H, act);
+    L.xq = L.has_xq ? take(moe::router_xq_bytes(Tc, s->H)) : 0;
     L.total = off;
     return L;
 }
@@ -285,6 +300,7 @@ int route_pass(const moe_shape_t *s, const moe_weights_t *w, const void *x, int 
     r.act = s->act_dtype == MOE_BF16 ? moe::ACT_BF16 : moe::ACT_F32;
     const bool small = moe::route_small_ok(Tc, s->top_k, s->E, s->H, r.act);
     r.ticket = small ? (int32_t *)(ws + L.blk) : nullptr;
+    r.xq = small && L.has_xq ? (uint8_t *)(ws + L.xq) : nullptr;
     // the segmented router counts the permutation's block histogram itself
     const bool seg = !small && moe::router_parts(Tc, s->H, s->E, r.act) == 8;
     r.hist = seg ? (int32_t *)(ws + L.blk) : nullptr;
@@ -410,9 +426,11 @@ int moe_forward(const moe_shape_t *s, const moe_weights_t *w, const void *x, voi
             d.topk_w = wts;
             d.h = wsb + Lw.h;
             d.y = yc;
+            d.xq = Lw.has_xq ? (const uint8_t *)(wsb + Lw.xq) : nullptr;
             if (moe::gate_up_mxfp4_pair_ok(d)) {
                 moe::RouterArgs r{};
                 r.x = xc;
+                r.xq = const_cast<uint8_t *>(d.xq);
                 r.wr = w->router_w;
                 r.bias = w->router_bias;
                 r.logits = (float *)(wsb + Lw.logits);
@@ -449,6 +467,10 @@ int moe_forward(const moe_shape_t *s, const moe_weights_t *w, const void *x, voi
         moe::ExpertArgs a = expert_shape(s, n);
         a.shape_T = Tc;
         a.x = xc;
+        // rows quantised by the short-pass router (route_pass set them up)
+        a.xq = Lw.has_xq && moe::route_small_ok(n, s->top_k, s->E, s->H, a.act)
+                   ? (const uint8_t *)(wsb + Lw.xq)
+                   : nullptr;
         a.w_gate = w->w_gate;
         a.w_up = w->w_up;
         a.w_down = w->w_down;

@@ -34,6 +34,7 @@
 // applies to row (column) r and K block b.
 #include "common.h"
 #include "kernels.h"
+#include "mxfp8.h"
 #include "topk.h"
 
 #include <algorithm>
@@ -45,10 +46,9 @@ int mxfp4_bm() { return 16; }
 
 namespace {
 
-constexpr int MX_PAD = 16;     // LDS row padding (bytes): rows fall on distinct banks
-
 struct MxP {
     const uint16_t *a;           // GU: x [T, H]; DC: h [rows, ldh]
+    const uint8_t *xq;           // GU: x quantised once per token (mxfp8.h records), or null
     const uint8_t *c0, *c1;      // codes [E, N, K/2]
     const uint8_t *s0, *s1;      // scales [E, N, K/32]
     const int32_t *row_tok, *offsets;
@@ -57,97 +57,6 @@ struct MxP {
     const int32_t *ntiles;
     int T, H, E, k, I, ldh, cap;
 };
-
-// E4M3 (OCP, bias 7) encoding of |v| <= 448, round to nearest even; both the
-// normal and the subnormal candidate are formed and one is selected, so the
-// conversion has no branch.
-__device__ __forceinline__ uint32_t e4m3(float v, float &q)
-{
-    const uint32_t sgn = (__float_as_uint(v) >> 24) & 0x80u;
-    const float a = fabsf(v);
-    // normal (2^-6 and up): round the fp32 mantissa to 3 bits
-    uint32_t u = __float_as_uint(a);
-    u = (u + 0x7FFFFu + ((u >> 20) & 1u)) & ~0xFFFFFu;
-    uint32_t cn = ((((u >> 23) - 127u + 7u) & 0xFu) << 3) | ((u >> 20) & 7u);
-    float mn = __uint_as_float(u);
-    const bool sat = u > 0x43E00000u;  // above 448
-    cn = sat ? 0x7Eu : cn;
-    mn = sat ? 448.0f : mn;
-    // subnormal: multiples of 2^-9 (8 encodes 2^-6, the smallest normal)
-    const float ns = rintf(a * 512.0f);
-    const bool normal = a >= 0.015625f;
-    const uint32_t code = normal ? cn : (uint32_t)ns;
-    const float mag = normal ? mn : ns * (1.0f / 512.0f);
-    q = sgn ? -mag : mag;
-    return sgn | code;
-}
-
-// Activation staging: the tile's rows are quantised into LDS, one 32-element
-// block per thread and pass, as hi / lo E4M3 bytes [row][K + MX_PAD] and
-// their E8M0 scales [row][K/32].  A block travels packed (16 registers) and
-// is converted 8 elements at a time.
-__device__ __forceinline__ void block_load(uint4 (&raw)[4], const uint16_t *src)
-{
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-        raw[c] = *(const uint4 *)(src + c * 8);
-}
-
-// Source of staging block q: row q / nblk (index src[row] of the activation
-// matrix), 32 elements at (q % nblk) * 32.
-__device__ __forceinline__ const uint16_t *block_src(const uint16_t *a, const u32v<4> &src,
-                                                    int64_t lda, int nblk, int q)
-{
-    const int r = q / nblk;
-    uint32_t s = src[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i)
-        s = r == i ? src[i] : s;
-    return a + (int64_t)s * lda + (q - r * nblk) * 32;
-}
-
-__device__ __forceinline__ void block_quantise(const uint4 (&raw)[4], int r, int b, int K,
-                                               uint8_t *ahi, uint8_t *alo, uint8_t *shi,
-                                               uint8_t *slo)
-{
-    const int nblk = K / 32, ld = K + MX_PAD;
-    // |bf16| maxima: with the sign bit cleared the bit patterns compare as
-    // the magnitudes do
-    uint32_t mx = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const uint32_t w4[4] = {raw[c].x, raw[c].y, raw[c].z, raw[c].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            mx = max(mx, max(w4[i] & 0x7FFFu, (w4[i] >> 16) & 0x7FFFu));
-    }
-    int e = (int)(mx >> 7) - 127 - 7;  // floor(log2 amax) - 7
-    if (mx == 0)
-        e = 0;
-    e = max(e, -123);
-    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
-    uint8_t *dh = ahi + r * ld + b * 32;
-    uint8_t *dl = alo + r * ld + b * 32;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const uint32_t w4[4] = {raw[c].x, raw[c].y, raw[c].z, raw[c].w};
-        uint32_t hi[2] = {0, 0}, lo[2] = {0, 0};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint16_t h = (uint16_t)(i & 1 ? w4[i / 2] >> 16 : w4[i / 2] & 0xFFFF);
-            float qh, ql;
-            const float xs = bf2f(h) * inv;
-            const uint32_t ch = e4m3(xs, qh);
-            const uint32_t cl = e4m3((xs - qh) * 16.0f, ql);
-            hi[i / 4] |= ch << (8 * (i % 4));
-            lo[i / 4] |= cl << (8 * (i % 4));
-        }
-        *(uint2 *)(dh + 8 * c) = uint2{hi[0], hi[1]};
-        *(uint2 *)(dl + 8 * c) = uint2{lo[0], lo[1]};
-    }
-    shi[r * nblk + b] = (uint8_t)(e + 127);
-    slo[r * nblk + b] = (uint8_t)(e - 4 + 127);
-}
 
 // A lane's weights of one K slab of NQ 128-wide steps, for one column block
 // and matrix, from the packed layout: step s is 16 bytes of a contiguous
@@ -325,6 +234,41 @@ __global__ __launch_bounds__(64 * NW, WF ? 2 : 3) void expert_mxfp4(MxP p, const
             block_load(raw0, block_src(p.a, src, lda, nblk, q));
             block_quantise(raw0, q / nblk, q % nblk, K, ahi, alo, shi, slo);
         }
+    } else if (GU && p.xq) {
+        // The router quantised every token row once: copy the tile rows'
+        // records into LDS, PB 16-byte pieces per thread at a time (decode
+        // and verify tiles hold a few rows: one or two rounds; four when the
+        // slice pointers stay live over K slabs).
+        constexpr int PB = ONE ? 8 : 4;
+        const int per = mx_rec_pieces(K), total = nrows * per;
+        for (int b0 = 0; b0 < total; b0 += PB * 64 * NW) {
+            uint4 pv[PB];
+#pragma unroll
+            for (int i = 0; i < PB; ++i) {
+                const int q = b0 + tid + 64 * NW * i;
+                const int r = q / per;
+                int goff;
+                uint8_t *dst;
+                mx_rec_piece(q - r * per, K, r, ahi, alo, shi, slo, goff, dst);
+                uint32_t tok = src[0];  // src[r] by selects: a vector indexed at run time
+#pragma unroll                          // would be placed in scratch memory
+                for (int k2 = 1; k2 < 16; ++k2)
+                    tok = r == k2 ? src[k2] : tok;
+                if (q < total)
+                    pv[i] = *(const uint4 *)(p.xq + (int64_t)tok * mx_row_bytes(K) + goff);
+            }
+#pragma unroll
+            for (int i = 0; i < PB; ++i) {
+                const int q = b0 + tid + 64 * NW * i;
+                const int r = q / per;
+                int goff;
+                uint8_t *dst;
+                mx_rec_piece(q - r * per, K, r, ahi, alo, shi, slo, goff, dst);
+                if (q < total)
+                    *(uint4 *)dst = pv[i];
+            }
+        }
+        issue_weights();
     } else {
         {
             uint4 raw0[4], raw1[4];
@@ -410,6 +354,7 @@ __global__ __launch_bounds__(64 * NW, WF ? 2 : 3) void expert_mxfp4(MxP p, const
 // quantised first and three fit.
 struct MxPairP {
     const uint16_t *x;            // [T, H]
+    const uint8_t *xq;            // x quantised once per token (mxfp8.h records), or null
     const float *logits;          // [T, E]
     const uint8_t *c0, *c1;       // gate / up codes, packed
     const uint8_t *s0, *s1;       // their scales, packed
@@ -419,8 +364,12 @@ struct MxPairP {
     int T, H, E, k, I;
 };
 
-template <int NW, int NQ, int PER, bool WF>
-__global__ __launch_bounds__(64 * NW, WF ? 2 : 3) void expert_mxfp4_pair(MxPairP p)
+// PRE: the router quantised the token's row already (one record per token,
+// shared by all its pairs and column blocks); the workgroup copies it into
+// LDS - requested with the logits, stored once the weights are requested -
+// instead of quantising the bf16 row itself.
+template <int NW, int NQ, int PER, bool WF, bool PRE>
+__global__ __launch_bounds__(64 * NW, (WF && !PRE) ? 2 : 3) void expert_mxfp4_pair(MxPairP p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int pr = blockIdx.y, t = pr / p.k, j = pr - t * p.k;
@@ -435,8 +384,22 @@ __global__ __launch_bounds__(64 * NW, WF ? 2 : 3) void expert_mxfp4_pair(MxPairP
         v[i] = lane + 64 * i < p.E ? p.logits[(int64_t)t * p.E + lane + 64 * i] : 0.0f;
     const uint16_t *xrow = p.x + (int64_t)t * p.H;
     uint4 raw[4];
-    if (tid < nblk)
+    constexpr int PP = (mx_rec_pieces(2048) + 64 * NW - 1) / (64 * NW);  // pieces per thread, K <= 2048
+    uint4 rp[PRE ? PP : 1];
+    if (PRE) {
+        const uint8_t *rec = p.xq + (int64_t)t * mx_row_bytes(K);
+#pragma unroll
+        for (int i = 0; i < PP; ++i) {
+            const int pc = tid + 64 * NW * i;
+            int goff;
+            uint8_t *dst;
+            mx_rec_piece(pc, K, 0, ahi, alo, shi, slo, goff, dst);
+            if (pc < mx_rec_pieces(K))
+                rp[i] = *(const uint4 *)(rec + goff);
+        }
+    } else if (tid < nblk) {
         block_load(raw, xrow + tid * 32);
+    }
     auto quantise = [&]() {
         if (tid < nblk)
             block_quantise(raw, 0, tid, K, ahi, alo, shi, slo);
@@ -446,7 +409,7 @@ __global__ __launch_bounds__(64 * NW, WF ? 2 : 3) void expert_mxfp4_pair(MxPairP
             block_quantise(r2, 0, q, K, ahi, alo, shi, slo);
         }
     };
-    if (!WF)
+    if (!WF && !PRE)
         quantise();
 
     // The pair's expert: rank j of the token's selection (every wave selects).
@@ -466,8 +429,19 @@ __global__ __launch_bounds__(64 * NW, WF ? 2 : 3) void expert_mxfp4_pair(MxPairP
                        s, s + 1);
         __builtin_amdgcn_sched_barrier(0);  // keep the issue order
     }
-    if (WF)
+    if (PRE) {
+#pragma unroll
+        for (int i = 0; i < PP; ++i) {
+            const int pc = tid + 64 * NW * i;
+            int goff;
+            uint8_t *dst;
+            mx_rec_piece(pc, K, 0, ahi, alo, shi, slo, goff, dst);
+            if (pc < mx_rec_pieces(K))
+                *(uint4 *)dst = rp[i];
+        }
+    } else if (WF) {
         quantise();
+    }
     if (j == 0 && blockIdx.x == 0 && wave == 0)
         wave_topk_weights(my_e, my_k, p.k, p.idx + (int64_t)t * p.k, p.w + (int64_t)t * p.k,
                           nullptr);
@@ -665,6 +639,7 @@ void run(const ExpertArgs &a, hipStream_t st)
 {
     MxP p;
     p.a = (const uint16_t *)(GU ? a.x : a.h);
+    p.xq = GU ? a.xq : nullptr;
     p.c0 = (const uint8_t *)(GU ? a.w_gate : a.w_down);
     p.c1 = (const uint8_t *)(GU ? a.w_up : nullptr);
     p.s0 = GU ? a.s_gate : a.s_down;
@@ -782,14 +757,15 @@ namespace {
 template <int NQ, int PER>
 void pair_launch(const MxPairP &p, hipStream_t st)
 {
-    const size_t lds = 2 * (size_t)(p.H + MX_PAD) + 2 * (size_t)(p.H / 32);
+    const size_t lds = (size_t)mx_row_bytes(p.H);
     constexpr int NW = 2;
     const dim3 grid(p.I / (16 * NW), p.T * p.k);
-    // a single row: weights first (the grid is far smaller than the chip)
-    if (p.T == 1)
-        expert_mxfp4_pair<NW, NQ, PER, true><<<grid, 64 * NW, lds, st>>>(p);
+    if (p.xq)  // quantised rows from the router: weights requested before the row lands
+        expert_mxfp4_pair<NW, NQ, PER, true, true><<<grid, 64 * NW, lds, st>>>(p);
+    else if (p.T == 1)  // a single row: weights first (the grid is far smaller than the chip)
+        expert_mxfp4_pair<NW, NQ, PER, true, false><<<grid, 64 * NW, lds, st>>>(p);
     else
-        expert_mxfp4_pair<NW, NQ, PER, false><<<grid, 64 * NW, lds, st>>>(p);
+        expert_mxfp4_pair<NW, NQ, PER, false, false><<<grid, 64 * NW, lds, st>>>(p);
 }
 
 template <int NQ>
@@ -818,6 +794,7 @@ void launch_gate_up_mxfp4_pair(const ExpertArgs &a, const float *logits, hipStre
 {
     MxPairP p;
     p.x = (const uint16_t *)a.x;
+    p.xq = a.xq;
     p.logits = logits;
     p.c0 = (const uint8_t *)a.w_gate;
     p.c1 = (const uint8_t *)a.w_up;

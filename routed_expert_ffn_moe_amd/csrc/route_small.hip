@@ -20,6 +20,7 @@
 // cut from nine dispatches to one; verify rows are 6 at a time).
 #include "common.h"
 #include "kernels.h"
+#include "mxfp8.h"
 #include "topk.h"
 
 namespace moe {
@@ -29,12 +30,19 @@ constexpr int RS_RING = 8;  // K steps in flight per wave
 // RW waves split K in RW equal parts (RW * 32 dividing H); for H = 2048 and
 // RW = 8 every wave's whole share is in flight at once.  Grid: (E / 16,
 // ceil(T / 16)).
+// With xrec set (MXFP4 experts), the workgroups also quantise the token rows
+// of their token block once for every expert kernel that reads them: row t
+// as a record of mx_row_bytes(H) bytes at xrec + t * mx_row_bytes(H) (hi, lo,
+// hi scales, lo scales: the LDS staging layout of one row), the 32-element
+// blocks dealt over the workgroups of the token block; the loads go out with
+// the router's own and the conversion follows its logits.
 template <int RW>
 __global__ __launch_bounds__(64 * RW) void router_small(const uint16_t *__restrict__ x,
                                                         const uint16_t *__restrict__ wr,
                                                         const float *__restrict__ bias,
                                                         float *__restrict__ logits,
-                                                        int32_t *__restrict__ ticket, int T, int H,
+                                                        int32_t *__restrict__ ticket,
+                                                        uint8_t *__restrict__ xrec, int T, int H,
                                                         int E)
 {
     __shared__ float red[RW][16][17];
@@ -43,6 +51,14 @@ __global__ __launch_bounds__(64 * RW) void router_small(const uint16_t *__restri
     const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
     if (ticket && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0)
         *ticket = 0;  // the route kernel after this one counts on it
+    // this thread's block of the token block's rows: (row qr, block qb)
+    const int nblk = H / 32;
+    const int qi = tid * gridDim.x + blockIdx.x;
+    const int qr = qi / nblk, qb = qi - qr * nblk;
+    const bool quant = xrec && qr < 16 && t0 + qr < T;
+    uint4 raw[4];
+    if (quant)
+        block_load(raw, x + (int64_t)(t0 + qr) * H + qb * 32);
     const int kq = H / RW;  // K share of this wave (multiple of 32)
     const uint16_t *wp = wr + (int64_t)min(e0 + l16, E - 1) * H + wave * kq + lg * 8;
     const uint16_t *xp = x + (int64_t)min(t0 + l16, T - 1) * H + wave * kq + lg * 8;
@@ -84,6 +100,11 @@ __global__ __launch_bounds__(64 * RW) void router_small(const uint16_t *__restri
                 v += red[w][er][tid & 15];
             logits[(int64_t)t * E + e] = v + (bias ? bias[e] : 0.0f);
         }
+    }
+    if (quant) {
+        uint8_t *rec = xrec + (int64_t)(t0 + qr) * mx_row_bytes(H);
+        const int ld = H + MX_PAD;
+        block_quantise(raw, 0, qb, H, rec, rec + ld, rec + 2 * ld, rec + 2 * ld + nblk);
     }
 }
 
@@ -265,6 +286,13 @@ bool route_small_ok(int T, int k, int E, int H, int act)
     return T <= 16 || router_small_rw(E, H, act) > 0;
 }
 
+bool router_xq_ok(int E, int H, int act)
+{
+    return router_small_rw(E, H, act) > 0 && H % 512 == 0;
+}
+
+size_t router_xq_bytes(int T, int H) { return (size_t)T * mx_row_bytes(H); }
+
 int router_small_rw(int E, int H, int act)
 {
     if (act != ACT_BF16 || E % 16 != 0)
@@ -278,11 +306,11 @@ void launch_router_small(const RouterArgs &r, hipStream_t st)
     switch (router_small_rw(r.E, r.H, r.act)) {
     case 8:
         router_small<8><<<grid, 512, 0, st>>>((const uint16_t *)r.x, (const uint16_t *)r.wr, r.bias,
-                                              r.logits, r.ticket, r.T, r.H, r.E);
+                                              r.logits, r.ticket, r.xq, r.T, r.H, r.E);
         break;
     case 4:
         router_small<4><<<grid, 256, 0, st>>>((const uint16_t *)r.x, (const uint16_t *)r.wr, r.bias,
-                                              r.logits, r.ticket, r.T, r.H, r.E);
+                                              r.logits, r.ticket, r.xq, r.T, r.H, r.E);
         break;
     default:
         launch_router_logits(r, st);  // one route workgroup only: no ticket

@@ -380,6 +380,40 @@ def test_mxfp4_prefill_matches_bf16_on_the_same_weights():
               hx.rel_err(hx.y_host(y4, "bf16"), hx.y_host(y16, "bf16")), "bf16")
 
 
+@pytest.mark.parametrize("T,hot", [(1, False), (6, False), (40, True), (64, False)])
+def test_mxfp4_rows_quantised_once_by_the_router(T, hot):
+    """With MOE_MX_XQ=1 the short-pass router quantises every token row once
+    (hi / lo MXFP8 records) and the MXFP4 gate+up kernels copy those records
+    instead of quantising their rows themselves: the same quantiser, so y,
+    the indices and the weights are bit-identical to the default path, for
+    the pair kernel (T=1, 6) and the grouped one (T=40 with full 16-row
+    tiles, T=64)."""
+    import os
+    say("[xq] T =", T, "hot" if hot else "")
+    c, g = layer("c4_t6")
+    c = dict(c, T=T, seed=9000 + T)
+    lay, gl = g.lay, g
+    if hot:
+        bias = np.zeros(c["E"], np.float32)
+        for r, e in enumerate([3, 17, 64, 65, 130, 200, 254, 255]):
+            bias[e] = 100.0 - 10.0 * r
+        lay = mi.LayerData(c=c, router_w=g.lay.router_w, router_bias=bias, w_gate=g.lay.w_gate,
+                           w_up=g.lay.w_up, w_down=g.lay.w_down, s_gate=g.lay.s_gate,
+                           s_up=g.lay.s_up, s_down=g.lay.s_down)
+        gl = hx.GpuLayer(c, lay)
+    xd = hx.act_torch(hx.margin_x(c, lay), c["act"], "cuda")
+    n0 = moe.moe_workspace_bytes(gl.shape(T))
+    y0, i0, w0 = gl.forward(xd)
+    os.environ["MOE_MX_XQ"] = "1"
+    try:
+        assert moe.moe_workspace_bytes(gl.shape(T)) > n0  # room for the row records
+        y1, i1, w1 = gl.forward(xd, poison=True)
+    finally:
+        del os.environ["MOE_MX_XQ"]
+    assert torch.equal(i0, i1) and torch.equal(w0, w1)
+    assert torch.equal(y0, y1)
+
+
 @pytest.mark.parametrize("T", [5, 100])
 def test_shared_expert_short_passes(T):
     """The shared expert (group E, every token) through the short-pass
