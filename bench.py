@@ -479,7 +479,7 @@ def small_t_sweep(steps, warmup, Ts=SMALL_T):
     return {"layer": "H=2048 E=256 top-8 I=768, MXFP4 experts, 16 weight sets", "points": out}
 
 
-SWEEP_T = (128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768)
+SWEEP_T = (128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768, 65536)
 
 
 def sweep(steps, warmup, Ts=SWEEP_T):

@@ -31,7 +31,14 @@ __device__ __forceinline__ uint32_t pack_bf2(float a, float b)
     return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU, z * sigmoid(z), with the hardware reciprocal (1 ulp) in place of an
+// IEEE division: the result is rounded to bf16 right after, and the
+// division's scaling and fix-up steps cost ten instructions per element in
+// the GEMM epilogues.
+__device__ __forceinline__ float silu(float z)
+{
+    return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // Token row and routing weight of a grouped row.  Pairs p < n_pairs are the
 // routed (t, j) pairs p = t * k + j; p >= n_pairs are shared-expert rows of
