@@ -1,8 +1,8 @@
 // Weight-streaming grouped expert GEMM on bf16 MFMA (gfx950).
 //
 // Same contract as the tiled kernel in expert_gemm.hip (gate+up with the
-// SwiGLU epilogue, or down with the routing-weight scale into per-pair
-// staging rows); built for the shapes of this layer, where every workload sits
+// SwiGLU epilogue, or down into per-pair staging rows, unscaled: the combine
+// applies the routing weights); built for the shapes of this layer, where every workload sits
 // below the bf16 ridge point and the expert weights are the traffic that
 // matters ("MoE prefill quantum", Table 9 and the text after it: small chunks
 // read nearly every expert's weights for a few rows each).
