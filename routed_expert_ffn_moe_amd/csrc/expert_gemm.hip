@@ -270,10 +270,24 @@ __global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__
     const int n_rows = k + (shared ? 1 : 0);  // <= KM
     int64_t row[KM];
     float w[KM];
+    if (per_row % 256 == 0) {
+        // a workgroup lies within one token: its rows and weights are
+        // uniform and come as scalar loads, off the vector memory path
+        const int tu = __builtin_amdgcn_readfirstlane(t);
 #pragma unroll
-    for (int j = 0; j < KM; ++j) {
-        row[j] = j < k ? row_of[(int64_t)t * k + j] : (int64_t)T * k + t;
-        w[j] = j < k ? topk_w[(int64_t)t * k + j] : 1.0f;
+        for (int j = 0; j < KM; ++j) {
+            row[j] = j < k ? __builtin_amdgcn_readfirstlane(row_of[(int64_t)tu * k + j])
+                           : (int64_t)T * k + tu;
+            w[j] = j < k ? __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                         __builtin_bit_cast(int, topk_w[(int64_t)tu * k + j])))
+                         : 1.0f;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+            row[j] = j < k ? row_of[(int64_t)t * k + j] : (int64_t)T * k + t;
+            w[j] = j < k ? topk_w[(int64_t)t * k + j] : 1.0f;
+        }
     }
     uint4 v[KM];
 #pragma unroll
