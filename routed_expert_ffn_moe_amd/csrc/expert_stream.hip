@@ -10,7 +10,10 @@
 //  * Each wave owns 32 weight rows per matrix (gate+up: two matrices) or 64
 //    (down) and streams them from HBM straight into registers through a
 //    prefetch ring of 4 or 8 steps of 32 K: no LDS and no barrier on the
-//    weight path, every weight element read once per tile.  The weights are
+//    weight path, every weight element read once per tile.  Wide tiles
+//    (128 token rows, for passes with 128 or more rows per expert on
+//    average) give each wave twice the weight rows, their accumulators all
+//    256 AGPRs, and a ring of 2 steps (as many MFMA cycles as 4 narrow ones).  The weights are
 //    in the packed layout (moe_pack_bf16): one K step of a 16-row block is a
 //    contiguous kilobyte, so each load instruction of a wave fetches whole
 //    cache lines (row-major rows would give 64 bytes of each of 16 lines).
@@ -52,8 +55,9 @@ namespace {
 // distinct banks.
 constexpr int sld_of(int skc) { return skc + 8; }
 // Weight rows per work item and matrix: 4 waves x 32 (gate+up, two
-// matrices) or 4 waves x 64 (down, one matrix).
-constexpr int wrows_of(bool gu) { return gu ? 128 : 256; }
+// matrices) or 4 waves x 64 (down, one matrix); twice that in the wide
+// tiles, whose 128-row accumulators take all 256 accumulation registers.
+constexpr int wrows_of(bool gu, bool wide) { return (gu ? 128 : 256) * (wide ? 2 : 1); }
 
 struct StreamP {
     const uint16_t *x;        // GU: activations [T, H]; DC: h [rows, ldh]
@@ -217,6 +221,44 @@ __device__ __forceinline__ void kchunk(bool full, const uint16_t *As, int slot0,
     }
 }
 
+// The wide tiles' K steps (accumulators in AGPRs, NMB token blocks).  The
+// MFMAs of a step go weight fragment by weight fragment, all token blocks of
+// one fragment back to back, and a fragment's ring slot is refilled right
+// after its last MFMA: the ring then needs no second copy of the fragments
+// in use, for which the 256 accumulators of a wide tile leave no registers.
+// A refill still lands SD steps ahead of its use.
+template <int NMB, int MB, int NB, int CB, int SD, int SKC>
+__device__ __forceinline__ void kchunk_wide(const uint16_t *As, int slot0, int l16, int lg,
+                                            uint4 (&bq)[SD][NB][CB],
+                                            const uint16_t *const (&wl)[3][NB],
+                                            const int (&woff)[CB], floatx4 (&acc)[NB][CB][MB])
+{
+    constexpr int SPC = SKC / 32, SLD = sld_of(SKC);
+    static_assert((SPC - 1 + SD) / SPC <= 2, "refills reach at most two chunks ahead");
+    bf16x8 tf[2][NMB];
+    frag_load<NMB, SLD>(tf[0], As, 0, l16, lg, true);
+#pragma unroll
+    for (int st = 0; st < SPC; ++st) {
+        const int slot = (slot0 + st) % SD;
+        const uint16_t *const *w = wl[(st + SD) / SPC];
+        const int wk = ((st + SD) % SPC) * 32;
+        if (st + 1 < SPC)
+            frag_load<NMB, SLD>(tf[(st + 1) & 1], As, st + 1, l16, lg, true);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const bf16x8 wf = as_bf16x8(bq[slot][m][cb]);
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb)
+                    mfma16_acc(acc[m][cb][mb], wf, tf[st & 1][mb]);
+                bq[slot][m][cb] = wload<false>(w[m] + woff[cb] + wk * 32);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+    }
+}
+
 // MXFP4 weights: 8 E2M1 codes (K = 8 consecutive elements, low nibble
 // first) times 2^(scale - 127) as a bf16 MFMA operand; the conversion takes
 // the E8M0 scale as the exponent field of an fp32.
@@ -315,20 +357,21 @@ __device__ __forceinline__ void kchunk_w4(bool full, const uint16_t *As, int slo
 // the LDS and L2 latency that one wave's own schedule cannot.
 constexpr int wg_per_cu(int bm) { return bm <= 16 ? 3 : bm <= 64 ? 2 : 1; }
 
-template <int BM, bool GU, int SD, int SKC, bool W4, int TL>
+template <int BM, bool GU, int SD, int SKC, bool W4, int TL, bool WIDE>
 __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
                                                                     const int4 *__restrict__ items)
 {
     constexpr int SLD = sld_of(SKC), SPC = SKC / 32, RW = SKC / 8;  // 16-byte pieces per row
     constexpr int NB = GU ? 2 : 1;             // weight matrices
-    constexpr int CB = GU ? 2 : 4;             // 16-row weight blocks per wave and matrix
+    constexpr int CB = (GU ? 2 : 4) * (WIDE ? 2 : 1);  // 16-row weight blocks per wave and matrix
     constexpr int MB = BM / 16;                // 16-row token blocks
     constexpr int ACH = BM * (SKC / 8) / 256;  // 16-byte token chunks per thread
-    static_assert(W4 || SD == 4 || SD == 8, "prefetch ring depth in K steps");
+    static_assert(W4 || SD == 4 || SD == 8 || (WIDE && SD == 2), "prefetch ring depth in K steps");
+    static_assert(!WIDE || (BM == 128 && !W4), "wide tiles: 128 bf16 rows");
     static_assert(W4 || (2 * SPC) % SD == 0, "ring slots line up with chunk pairs");
     static_assert(!W4 || (SD == 2 && SKC == 128), "MXFP4: a ring of two 128-K chunks");
     static_assert(ACH >= 1 && ACH * 256 == BM * SKC / 8, "token staging");
-    static_assert(CB % 2 == 0 && 4 * CB * 16 == wrows_of(GU), "column blocks go in pairs");
+    static_assert(CB % 2 == 0 && 4 * CB * 16 == wrows_of(GU, WIDE), "column blocks go in pairs");
     // the 128-row tiles' accumulators fill the accumulation registers
     constexpr bool AGPR = BM >= 128;
 
@@ -491,7 +534,14 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
                     // Items whose rows fit the first half of the row tile skip
                     // the MFMAs of the second half (the tile's other empty row
                     // blocks are computed: finer splits cost more than they save).
-                    kchunk<MB, NB, CB, SD, SKC, AGPR>(full, As, h * SPC, l16, lg, bq, wl, woff, acc);
+                    // (the wide tiles always run every MFMA: a second
+                    // instantiation for half-filled tiles costs their
+                    // accumulators a round of copies at each branch)
+                    if (WIDE)
+                        kchunk_wide<MB, MB, NB, CB, SD, SKC>(As, h * SPC, l16, lg, bq, wl, woff, acc);
+                    else
+                        kchunk<MB, NB, CB, SD, SKC, AGPR>(full, As, h * SPC, l16, lg, bq, wl, woff,
+                                                          acc);
                 }
                 // Token chunk pipeline: rt[h % TL] holds the chunk after this
                 // one and is reloaded with the chunk TL + 1 ahead.
@@ -578,7 +628,19 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
     }
 }
 
-template <int BM, bool GU, int SD, int SKC, bool W4, int TL>
+// CUs of the current device (read once per process).
+int device_cus()
+{
+    static const int cus = [] {
+        int dev = 0, n = 0;
+        (void)hipGetDevice(&dev);
+        (void)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        return n > 0 ? n : 256;
+    }();
+    return cus;
+}
+
+template <int BM, bool GU, int SD, int SKC, bool W4, int TL, bool WIDE = false>
 void run(const ExpertArgs &a, hipStream_t st)
 {
     StreamP p;
@@ -605,24 +667,18 @@ void run(const ExpertArgs &a, hipStream_t st)
     p.Is = a.I_shared;
     p.ldh = a.I > a.I_shared ? a.I : a.I_shared;
     const int N = GU ? p.ldh : a.H;
-    p.ntn = (N + wrows_of(GU) - 1) / wrows_of(GU);
+    p.ntn = (N + wrows_of(GU, WIDE) - 1) / wrows_of(GU, WIDE);
     const int64_t items = (int64_t)p.ntn * (GU ? a.max_tiles_gu : a.max_tiles_dc);
     if (items == 0)
         return;
     // Persistent grid: as many workgroups per XCD as fit at once, never more
     // than the items an XCD can receive.
     static int per_cu[2] = {0, 0};
-    static int cus = 0;
-    if (!cus) {
-        int dev = 0, n = 0;
-        (void)hipGetDevice(&dev);
-        (void)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-        cus = n > 0 ? n : 256;
-    }
+    const int cus = device_cus();
     int &occ = per_cu[GU ? 1 : 0];
     if (!occ) {
         int b = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, expert_stream<BM, GU, SD, SKC, W4, TL>, 256,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, expert_stream<BM, GU, SD, SKC, W4, TL, WIDE>, 256,
                                                          0) != hipSuccess ||
             b < 1)
             b = 1;
@@ -630,7 +686,7 @@ void run(const ExpertArgs &a, hipStream_t st)
     }
     const int64_t per_xcd = (items + 7) / 8;
     const int64_t slots = std::min<int64_t>(per_xcd, (int64_t)(cus / 8) * occ);
-    expert_stream<BM, GU, SD, SKC, W4, TL><<<(unsigned)(slots * 8), 256, 0, st>>>(p, p.items);
+    expert_stream<BM, GU, SD, SKC, W4, TL, WIDE><<<(unsigned)(slots * 8), 256, 0, st>>>(p, p.items);
 }
 
 }  // namespace
@@ -653,18 +709,48 @@ bool stream_ok(const ExpertArgs &a, bool gu)
         return false;
     // K in an even number of at least four 128-wide chunks
     if (gu)
-        return a.H % 256 == 0 && a.H >= 512 && a.I % wrows_of(true) == 0;
-    return a.I % 256 == 0 && a.I >= 512 && a.H % wrows_of(false) == 0;
+        return a.H % 256 == 0 && a.H >= 512 && a.I % wrows_of(true, false) == 0;
+    return a.I % 256 == 0 && a.I >= 512 && a.H % wrows_of(false, false) == 0;
 }
 
-int stream_wrows(bool gu) { return wrows_of(gu); }
+// Wide tiles for the 128-row bf16 tiles when the experts hold 128 rows or
+// more on average, the weight slices divide N and the pass still deals out
+// at least 12 wide items per CU: per MFMA they read half the LDS bytes and
+// stage half the token bytes of the narrow tiles, but they always run the
+// whole tile's MFMAs and come in half as many items.  Measured (ms per
+// layer, narrow -> wide): the 384-expert top-6 layer at T=8192 (128 rows per
+// expert, ~26 items per CU) 4.96 -> 4.56; the 256-expert top-8 layer
+// (I=768) at T=16384 1.65 -> 1.55 and T=32768 3.07 -> 2.83, at T=8192
+// (~9 items per CU) 0.93 -> 0.95, at T=4096 (~6) 0.65 -> 0.68, at T=2048
+// with Zipf bias (64 rows per expert) 0.36 -> 0.38.  MOE_STREAM_WIDE (0 or
+// 1) overrides the rule for tuning runs and tests; it is read at each call,
+// so a workspace sized under one setting may be refused under the other.
+static bool stream_wide(const ExpertArgs &a, bool gu)
+{
+    const char *e = getenv("MOE_STREAM_WIDE");
+    const int forced = e && (e[0] == '0' || e[0] == '1') ? e[0] - '0' : -1;
+    if (forced == 0 || a.wdt != W_BF16 || stream_bm(a) != 128)
+        return false;
+    const int N = gu ? (a.I > a.I_shared ? a.I : a.I_shared) : a.H;
+    if (N % wrows_of(gu, true) != 0)
+        return false;
+    if (forced == 1)
+        return true;
+    const int64_t pairs = (int64_t)a.shape_T * a.k;
+    const int64_t tiles = pairs / 128 + a.E + (a.I_shared > 0 ? a.shape_T / 128 : 0);
+    return pairs >= 128 * (int64_t)a.E &&
+           tiles * (N / wrows_of(gu, true)) >= 12 * (int64_t)device_cus();
+}
+
+int stream_wrows(const ExpertArgs &a, bool gu) { return wrows_of(gu, stream_wide(a, gu)); }
 
 int stream_ntn(const ExpertArgs &a, bool gu)
 {
     if (!stream_ok(a, gu))
         return 0;
     const int N = gu ? (a.I > a.I_shared ? a.I : a.I_shared) : a.H;
-    return (N + wrows_of(gu) - 1) / wrows_of(gu);
+    const int wr = wrows_of(gu, stream_wide(a, gu));
+    return (N + wr - 1) / wr;
 }
 
 // Row-tile size by the mean rows per expert; MOE_STREAM_BM (16, 32, 64 or
@@ -747,6 +833,10 @@ static void run_skc(const ExpertArgs &a, hipStream_t st)
 template <int BM, bool GU>
 static void run_sd(const ExpertArgs &a, hipStream_t st)
 {
+    if (BM == 128 && stream_wide(a, GU)) {  // a ring of two K steps: as many cycles as four narrow ones
+        run<128, GU, 2, 128, false, 1, true>(a, st);
+        return;
+    }
     if (a.wdt == W_MXFP4) {  // a ring of two 128-K chunks of fp4 codes
         if (stream_tl_w4() == 1)
             run<BM, GU, 2, 128, true, 1>(a, st);

@@ -113,7 +113,7 @@ int gemm_bm_dc(const ExpertArgs &a);
 bool stream_ok(const ExpertArgs &a, bool gu);
 int stream_bm(const ExpertArgs &a);
 int stream_ntn(const ExpertArgs &a, bool gu);  // column tiles (0 if not streaming)
-int stream_wrows(bool gu);                     // weight rows per streaming work item
+int stream_wrows(const ExpertArgs &a, bool gu);  // weight rows per streaming work item
 void launch_stream(const ExpertArgs &a, bool gu, hipStream_t st);
 
 // MXFP4 expert weights (bf16 activations, no shared expert).

@@ -137,7 +137,7 @@ struct Layout {
     size_t logits, wts, blk, counts, offsets, row_src, row_tok, row_of, tiles_gu, ntiles, tiles_dc,
         items_gu, items_dc, h, stage, xq, total;
     bool has_xq;  // MXFP4 passes routed by router_small: x quantised once per token
-    int max_tiles_gu, max_tiles_dc, bm_gu, bm_dc, ntn_gu, ntn_dc;
+    int max_tiles_gu, max_tiles_dc, bm_gu, bm_dc, ntn_gu, ntn_dc, wrows_gu, wrows_dc;
 };
 
 moe::ExpertArgs expert_shape(const moe_shape_t *s, int Tc)
@@ -174,6 +174,8 @@ Layout layout(const moe_shape_t *s, int Tc)
     L.max_tiles_dc = max_tiles(Tc, s, L.bm_dc);
     L.ntn_gu = moe::stream_ntn(a, true);
     L.ntn_dc = moe::stream_ntn(a, false);
+    L.wrows_gu = moe::stream_wrows(a, true);
+    L.wrows_dc = moe::stream_wrows(a, false);
     const int64_t pairs = (int64_t)Tc * s->top_k;
     const int64_t rows = pairs + (s->I_shared > 0 ? Tc : 0);
     const int64_t ldh = std::max(s->I, s->I_shared);
@@ -336,8 +338,8 @@ int route_pass(const moe_shape_t *s, const moe_weights_t *w, const void *x, int 
     p.ntn_b = L.ntn_dc;
     p.max_tiles_a = L.max_tiles_gu;
     p.max_tiles_b = L.max_tiles_dc;
-    p.wrows_a = moe::stream_wrows(true);
-    p.wrows_b = moe::stream_wrows(false);
+    p.wrows_a = L.wrows_gu;
+    p.wrows_b = L.wrows_dc;
     p.T = Tc;
     p.E = s->E;
     p.k = s->top_k;

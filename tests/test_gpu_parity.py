@@ -437,7 +437,8 @@ def test_shared_expert_short_passes(T):
 # without the 16-expert tiles, router_gemm (E not a multiple of 128), the
 # tiled GEMMs where the streaming kernels do not apply (H % 256, I < 512, a
 # shared expert of another width), MXFP4 slabs of one 128-wide step and of 16
-# steps over a 4096-wide K, the segmented router with one expert block, fp32.
+# steps over a 4096-wide K, the segmented router with one expert block, fp32,
+# the streaming kernels' wide tiles.
 SWEEP = {
     "SA": dict(T=50, H=384, E=24, top_k=3, I=192, I_shared=0, act="bf16", w="bf16", bias=None),
     "SB": dict(T=200, H=1024, E=64, top_k=4, I=256, I_shared=0, act="bf16", w="bf16",
@@ -447,21 +448,52 @@ SWEEP = {
     "SE": dict(T=3, H=4096, E=16, top_k=2, I=512, I_shared=0, act="bf16", w="mxfp4", bias=None),
     "SF": dict(T=33, H=128, E=5, top_k=2, I=64, I_shared=0, act="f32", w="f32", bias=None),
     "SG": dict(T=300, H=2048, E=128, top_k=2, I=512, I_shared=0, act="bf16", w="bf16", bias=None),
+    # 128 rows per expert on average: the streaming kernels' wide tiles, with
+    # Zipf-skewed groups (full, partial and single-row tiles) and with a
+    # shared expert of the routed width
+    "SH": dict(T=1024, H=512, E=16, top_k=2, I=512, I_shared=0, act="bf16", w="bf16",
+               bias="zipf1.1"),
+    "SI": dict(T=640, H=1024, E=8, top_k=2, I=512, I_shared=512, act="bf16", w="bf16",
+               bias="uniform"),
 }
 
 
+# Tuning switches set around a shape's call (the library reads them at each
+# call): the wide tiles are forced on shapes too small to deal out enough
+# items for the library to pick them by itself.
+SWEEP_ENV = {"SH": {"MOE_STREAM_WIDE": "1"}, "SI": {"MOE_STREAM_WIDE": "1"}}
+
+
 @pytest.mark.parametrize("name", sorted(SWEEP))
-def test_shape_sweep(name):
-    say("[sweep]", name, SWEEP[name])
+def test_shape_sweep(name, monkeypatch):
+    say("[sweep]", name, SWEEP[name], SWEEP_ENV.get(name, {}))
     c = dict(SWEEP[name], layer=name, seed=5000 + ord(name[1]), desc=name)
     lay = mi.make_layer(c, "cuda")
     g = hx.GpuLayer(c, lay)
     x = hx.margin_x(c, lay)
+    for k, v in SWEEP_ENV.get(name, {}).items():
+        monkeypatch.setenv(k, v)
     y, idx, w = g.forward(hx.act_torch(x, c["act"], "cuda"))
     y_ref, idx_r, w_r = oracle.forward(hx.oracle_layer(c, lay), x)
     assert np.array_equal(idx.cpu().numpy(), idx_r)
     assert np.abs(w.cpu().numpy() - w_r).max() <= hx.W_TOL
     check_err("sweep %s" % name, hx.rel_err(hx.y_host(y, c["act"]), y_ref), c["w"])
+
+
+@pytest.mark.parametrize("name", ["SH", "SI"])
+def test_wide_tiles_match_narrow_tiles_bit_exactly(name, monkeypatch):
+    """Both tile widths run every output element's MFMAs over the same K
+    steps in the same order, so y must not differ in a single bit."""
+    c = dict(SWEEP[name], layer=name, seed=5000 + ord(name[1]), desc=name)
+    lay = mi.make_layer(c, "cuda")
+    g = hx.GpuLayer(c, lay)
+    xd = hx.act_torch(hx.margin_x(c, lay), c["act"], "cuda")
+    ys = []
+    for v in ("0", "1"):
+        monkeypatch.setenv("MOE_STREAM_WIDE", v)
+        y, _, _ = g.forward(xd, poison=True)
+        ys.append(y.view(torch.int16).cpu())
+    assert torch.equal(ys[0], ys[1])
 
 
 def test_zero_tokens_is_a_no_op():
