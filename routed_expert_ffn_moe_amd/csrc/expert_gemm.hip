@@ -293,7 +293,13 @@ __global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__
 #pragma unroll
     for (int j = 0; j < KM; ++j)
         if (j < n_rows)
-            v[j] = *(const uint4 *)(stage + row[j] * H + c8);
+        {
+            // each staging row is read once: non-temporal (T=8192 with a
+            // shared expert: 103.6 -> 91.8 us; T=2048: 16.5 -> 16.2 us)
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 t4 = __builtin_nontemporal_load((const u32x4 *)(stage + row[j] * H + c8));
+            v[j] = uint4{t4[0], t4[1], t4[2], t4[3]};
+        }
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < KM; ++j)
