@@ -223,6 +223,20 @@ class Workload:
         moe.moe_stage_timing_enable(False)
         return wall, {k: v / max(n, 1) for k, v in ms.items()}
 
+    def per_call(self, steps):
+        """Each call timed on its own with HIP events on the launch stream:
+        median, p10 and p90 in microseconds."""
+        torch = self.torch
+        st = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            a.record(st)
+            self.step()
+            b.record(st)
+        torch.cuda.synchronize()
+        return quantiles([a.elapsed_time(b) * 1e3 for a, b in ev])
+
     def time_graph(self, steps, warmup):
         """Per-step time with the whole layer replayed from HIP graphs (one
         graph per weight set), for launch-bound decode shapes."""
@@ -262,6 +276,72 @@ class Workload:
         import numpy as np
         idx = self.idx.cpu().numpy()
         return np.bincount(idx.reshape(-1), minlength=self.c["E"])
+
+
+def quantiles(us):
+    """Median, p10 and p90 (nearest rank) of a list of microsecond figures."""
+    v = sorted(us)
+    q = lambda f: v[min(len(v) - 1, int(round(f * (len(v) - 1))))]
+    return {"calls": len(v), "median": round(q(0.5), 2), "p10": round(q(0.1), 2),
+            "p90": round(q(0.9), 2)}
+
+
+def parse_clocks(text):
+    """(sclk MHz, mclk MHz) from one `rocm-smi --showclocks` listing (None
+    where a clock is not listed)."""
+    import re
+    out = {}
+    for name in ("sclk", "mclk"):
+        m = re.search(r"%s clock level:\s*\S+:?\s*\((\d+)\s*Mhz\)" % name, text, re.IGNORECASE)
+        out[name] = int(m.group(1)) if m else None
+    return out["sclk"], out["mclk"]
+
+
+def clock_log(run, seconds=2.0, period=0.25):
+    """Shader and memory clocks while `run(stop)` keeps the GPU busy for
+    `seconds`: `rocm-smi --showclocks` sampled every `period` seconds from a
+    child process; None where the tool is missing or lists no clocks."""
+    import shutil
+    import subprocess
+    import threading
+    tool = shutil.which("rocm-smi") or ("/opt/rocm/bin/rocm-smi"
+                                        if os.path.exists("/opt/rocm/bin/rocm-smi") else None)
+    if tool is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                r = subprocess.run([tool, "--showclocks"], capture_output=True, text=True,
+                                   timeout=5)
+                samples.append(parse_clocks(r.stdout))
+            except (OSError, subprocess.SubprocessError):
+                pass
+            stop.wait(period)
+
+    th = threading.Thread(target=sample, daemon=True)
+    t_end = time.perf_counter() + seconds
+    th.start()
+    try:
+        run(lambda: time.perf_counter() >= t_end)
+    finally:
+        stop.set()
+        th.join()
+    # the first samples can fall before the load reaches the clocks
+    busy = samples[2:] if len(samples) > 4 else samples
+
+    def summary(vals):
+        vals = sorted(v for v in vals if v is not None)
+        if not vals:
+            return None
+        return {"min": vals[0], "median": vals[len(vals) // 2], "max": vals[-1],
+                "samples": len(vals)}
+    s_clk, m_clk = summary([a for a, _ in busy]), summary([b for _, b in busy])
+    if s_clk is None and m_clk is None:
+        return None
+    return {"sclk_mhz": s_clk, "mclk_mhz": m_clk, "tool": "rocm-smi --showclocks",
+            "window_s": seconds}
 
 
 def ceilings():
@@ -533,8 +613,11 @@ def sweep(steps, warmup, Ts=SWEEP_T):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 200 steps: a burst of calls after a synchronisation starts with ~10-20%
+    # slower calls for its first few milliseconds (the launch queue has not
+    # run ahead yet), which 50 steps of the 0.3 ms layer would still include
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--extra", default="c1,c3,c4_t6,c4_t1,c4_p2048",
                     help="comma-separated secondary workloads ('' for none)")
@@ -574,6 +657,14 @@ def main():
     steps = max(args.steps, 200 if c["T"] <= 8 else args.steps)
     wall, stages = wl.time(steps, args.warmup)
     gwall = wl.time_graph(steps, args.warmup) if c["T"] <= 16 else None
+    per_call = wl.per_call(steps)
+
+    def busy(done):
+        while not done():
+            for _ in range(10):
+                wl.step()
+            torch.cuda.synchronize()
+    clocks = clock_log(busy)
     d = describe(wl, wall, stages, steps, gwall)
     ms_step = wall / steps * 1e3
     out = {
@@ -598,6 +689,8 @@ def main():
         "grouped_gemms": d["grouped_gemms"],
         "overhead_bytes": d["overhead_bytes"],
         "stages_us": d["stages_us"],
+        "per_call_us": per_call,
+        "clocks": clocks,
         "weight_sets": d["weight_sets"],
         "ceilings": ceil,
         "tuning": {k: v for k, v in os.environ.items() if k.startswith("MOE_")},
@@ -614,7 +707,8 @@ def main():
         st = max(args.steps, 200 if cc["T"] <= 8 else args.steps)
         wall2, st2 = w2.time(st, args.warmup)
         g2 = w2.time_graph(st, args.warmup) if cc["T"] <= 16 else None
-        also[name] = {"workload": mi.cfg(name)["desc"], **describe(w2, wall2, st2, st, g2)}
+        also[name] = {"workload": mi.cfg(name)["desc"], **describe(w2, wall2, st2, st, g2),
+                      "per_call_us": w2.per_call(st)}
         del w2
         torch.cuda.empty_cache()
     out["also"] = also

@@ -107,3 +107,19 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_clock_listing_parse():
+    """sclk / mclk from the `rocm-smi --showclocks` listing format (levels
+    numbered or 'S' for the sleep state), and None where a clock is absent."""
+    line = ("GPU[0]\t\t: mclk clock level: 0: (2000Mhz) "
+            "GPU[0]\t\t: sclk clock level: 1: (2225Mhz) ")
+    assert bench.parse_clocks(line) == (2225, 2000)
+    assert bench.parse_clocks("GPU[0] : sclk clock level: S: (102Mhz)") == (102, None)
+    assert bench.parse_clocks("no clocks here") == (None, None)
+
+
+def test_per_call_quantiles():
+    q = bench.quantiles([float(v) for v in range(100, 0, -1)])  # 1..100 in any order
+    assert q == {"calls": 100, "median": 51.0, "p10": 11.0, "p90": 90.0}
+    assert bench.quantiles([7.0]) == {"calls": 1, "median": 7.0, "p10": 7.0, "p90": 7.0}
