@@ -75,6 +75,11 @@ int router_small_rw(int E, int H, int act);  // waves of router_small, 0 if it d
 bool router_xq_ok(int E, int H, int act);
 size_t router_xq_bytes(int T, int H);
 void launch_router_small(const RouterArgs &r, hipStream_t st);  // logits only
+// Decode rows: the eight K-segment partial sums of router_small's logits as
+// planes [8][T][E] at r.logits (no bias), for the decode gate+up kernel to
+// add (T <= 16, bf16, router_small with 8 waves applicable).
+bool router_split_ok(int T, int E, int H, int act);
+void launch_router_split(const RouterArgs &r, hipStream_t st);
 void launch_route_small(const RouterArgs &r, const PermuteArgs &a, hipStream_t st);  // top-k + permutation
 
 // Grouped gate+up GEMM with the SwiGLU epilogue: h[row] = silu(x_t Wg^T) *
@@ -130,7 +135,8 @@ void launch_down_combine_mxfp4(const ExpertArgs &a, hipStream_t st);  // row_of 
 // kernels), h in pair order, and the indices and weights into topk_idx /
 // topk_w.  Followed by launch_down_combine_mxfp4 with row_of null.
 bool gate_up_mxfp4_pair_ok(const ExpertArgs &a);
-void launch_gate_up_mxfp4_pair(const ExpertArgs &a, const float *logits, hipStream_t st);
+void launch_gate_up_mxfp4_pair(const ExpertArgs &a, const float *logits, const float *bias,
+                               int nparts, hipStream_t st);
 // OCP row-major MXFP4 (codes [E, N, K/2], scales [E, N, K/32]) into the
 // packed layout the MXFP4 kernels read.
 void launch_pack_mxfp4(int E, int N, int K, const uint8_t *codes, const uint8_t *scales,

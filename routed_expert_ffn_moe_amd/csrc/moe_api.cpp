@@ -138,6 +138,7 @@ struct Layout {
         items_gu, items_dc, h, stage, xq, total;
     bool has_xq;  // MXFP4 passes routed by router_small: x quantised once per token
     int max_tiles_gu, max_tiles_dc, bm_gu, bm_dc, ntn_gu, ntn_dc, wrows_gu, wrows_dc;
+    int64_t logit_floats;  // capacity of the logits area
 };
 
 moe::ExpertArgs expert_shape(const moe_shape_t *s, int Tc)
@@ -186,9 +187,14 @@ Layout layout(const moe_shape_t *s, int Tc)
         off = align256(off + bytes);
         return o;
     };
-    L.logits = take((size_t)Tc * s->E * 4 *
-                    moe::router_parts(Tc, s->H, s->E,
-                                      s->act_dtype == MOE_BF16 ? moe::ACT_BF16 : moe::ACT_F32));
+    // logits: one plane, or the eight partial-sum planes of the segmented
+    // router (long passes) or of the split router (decode rows)
+    const int ract = s->act_dtype == MOE_BF16 ? moe::ACT_BF16 : moe::ACT_F32;
+    const int nplanes = moe::router_split_ok(Tc, s->E, s->H, ract)
+                            ? 8
+                            : moe::router_parts(Tc, s->H, s->E, ract);
+    L.logit_floats = (int64_t)Tc * s->E * nplanes;
+    L.logits = take((size_t)L.logit_floats * 4);
     L.wts = take((size_t)pairs * 4);
     L.blk = take((size_t)std::max(1, moe::permute_blocks((int)pairs)) * s->E * 4);
     L.counts = take((size_t)(s->E + 1) * 4);
@@ -441,15 +447,21 @@ int moe_forward(const moe_shape_t *s, const moe_weights_t *w, const void *x, voi
                 r.E = s->E;
                 r.k = s->top_k;
                 r.act = moe::ACT_BF16;
+                // the split router unless the router also quantises x
+                const bool split = !d.xq && moe::router_split_ok(n, s->E, s->H, r.act) &&
+                                   (int64_t)8 * n * s->E <= Lw.logit_floats;
                 {
                     StageScope sc(0, st);
-                    moe::launch_router_small(r, st);
+                    if (split)
+                        moe::launch_router_split(r, st);
+                    else
+                        moe::launch_router_small(r, st);
                 }
                 if ((rc = launched("router")))
                     return rc;
                 {
                     StageScope sc(2, st);
-                    moe::launch_gate_up_mxfp4_pair(d, r.logits, st);
+                    moe::launch_gate_up_mxfp4_pair(d, r.logits, w->router_bias, split ? 8 : 1, st);
                 }
                 if ((rc = launched("gate_up")))
                     return rc;

@@ -355,13 +355,14 @@ __global__ __launch_bounds__(64 * NW, WF ? 2 : 3) void expert_mxfp4(MxP p, const
 struct MxPairP {
     const uint16_t *x;            // [T, H]
     const uint8_t *xq;            // x quantised once per token (mxfp8.h records), or null
-    const float *logits;          // [T, E]
+    const float *logits;          // [T, E], or with nparts 8 the router's planes [8][T, E]
+    const float *bias;            // [E] or null: added here when nparts is 8
     const uint8_t *c0, *c1;       // gate / up codes, packed
     const uint8_t *s0, *s1;       // their scales, packed
     uint16_t *h;                  // [T * k, I]: the row of pair t * k + j
     int32_t *idx;                 // [T, k]
     float *w;                     // [T, k]
-    int T, H, E, k, I;
+    int T, H, E, k, I, nparts;
 };
 
 // PRE: the router quantised the token's row already (one record per token,
@@ -377,11 +378,34 @@ __global__ __launch_bounds__(64 * NW, (WF && !PRE) ? 2 : 3) void expert_mxfp4_pa
     const int K = p.H, nblk = K / 32, ld = K + MX_PAD;  // K = NQ * 128
     uint8_t *ahi = smem, *alo = ahi + ld, *shi = alo + ld, *slo = shi + nblk;
 
-    // The token's logits and its activation row, requested together.
+    // The token's logits and its activation row, requested together.  From
+    // the split router's eight partial-sum planes the logit is their sum in
+    // plane order plus the bias, as router_small forms it.
     float v[PER];
+    if (p.nparts == 8) {
+        const int64_t plane = (int64_t)p.T * p.E;
+        float q[8][PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i)
-        v[i] = lane + 64 * i < p.E ? p.logits[(int64_t)t * p.E + lane + 64 * i] : 0.0f;
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int i = 0; i < PER; ++i)
+                q[s][i] = lane + 64 * i < p.E
+                              ? p.logits[s * plane + (int64_t)t * p.E + lane + 64 * i]
+                              : 0.0f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = lane + 64 * i;
+            float a = q[0][i];
+#pragma unroll
+            for (int s = 1; s < 8; ++s)
+                a += q[s][i];
+            v[i] = e < p.E ? a + (p.bias ? p.bias[e] : 0.0f) : 0.0f;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            v[i] = lane + 64 * i < p.E ? p.logits[(int64_t)t * p.E + lane + 64 * i] : 0.0f;
+    }
     const uint16_t *xrow = p.x + (int64_t)t * p.H;
     uint4 raw[4];
     constexpr int PP = (mx_rec_pieces(2048) + 64 * NW - 1) / (64 * NW);  // pieces per thread, K <= 2048
@@ -790,12 +814,15 @@ bool gate_up_mxfp4_pair_ok(const ExpertArgs &a)
            a.topk_w && a.y && (q == 1 || q == 2 || q == 4 || q == 6 || q == 8 || q == 16);
 }
 
-void launch_gate_up_mxfp4_pair(const ExpertArgs &a, const float *logits, hipStream_t st)
+void launch_gate_up_mxfp4_pair(const ExpertArgs &a, const float *logits, const float *bias,
+                               int nparts, hipStream_t st)
 {
     MxPairP p;
     p.x = (const uint16_t *)a.x;
     p.xq = a.xq;
     p.logits = logits;
+    p.bias = bias;
+    p.nparts = nparts;
     p.c0 = (const uint8_t *)a.w_gate;
     p.c1 = (const uint8_t *)a.w_up;
     p.s0 = a.s_gate;

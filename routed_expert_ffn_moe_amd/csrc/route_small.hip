@@ -108,6 +108,54 @@ __global__ __launch_bounds__(64 * RW) void router_small(const uint16_t *__restri
     }
 }
 
+// Decode rows (T <= 16: one token block): router_small's eight K-segment
+// waves as eight workgroups of one wave each, so that the router matrix is
+// read by eight times as many CUs.  Segment `seg` of expert block
+// blockIdx.x writes its partial sums to part[seg][t][e]; the decode gate+up
+// kernel adds the eight in segment order and then the bias, which is the
+// sum router_small forms in LDS (so the logits have the same bits).
+__global__ __launch_bounds__(64) void router_split(const uint16_t *__restrict__ x,
+                                                   const uint16_t *__restrict__ wr,
+                                                   float *__restrict__ part, int T, int H, int E)
+{
+    const int lane = threadIdx.x, l16 = lane & 15, lg = lane >> 4;
+    const int e0 = blockIdx.x * 16, seg = blockIdx.y;
+    const int kq = H / 8;  // K share of this segment (multiple of 32)
+    const uint16_t *wp = wr + (int64_t)min(e0 + l16, E - 1) * H + seg * kq + lg * 8;
+    const uint16_t *xp = x + (int64_t)min(l16, T - 1) * H + seg * kq + lg * 8;
+    const int nst = kq / 32;
+    uint4 wq[RS_RING], xq[RS_RING];
+#pragma unroll
+    for (int d = 0; d < RS_RING; ++d)
+        if (d < nst) {
+            wq[d] = *(const uint4 *)(wp + d * 32);
+            xq[d] = *(const uint4 *)(xp + d * 32);
+        }
+    floatx4 acc = {0, 0, 0, 0};
+    for (int s0 = 0; s0 < nst; s0 += RS_RING) {
+#pragma unroll
+        for (int d = 0; d < RS_RING; ++d) {
+            const int s = s0 + d;
+            if (s < nst) {
+                const bf16x8 wf = as_bf16x8(wq[d]), xf = as_bf16x8(xq[d]);
+                if (s + RS_RING < nst) {
+                    wq[d] = *(const uint4 *)(wp + (s + RS_RING) * 32);
+                    xq[d] = *(const uint4 *)(xp + (s + RS_RING) * 32);
+                }
+                acc = mfma16(wf, xf, acc);
+            }
+        }
+    }
+    // C[expert 4*lg + i][token l16]
+    if (l16 < T) {
+        float *dst = part + ((int64_t)seg * T + l16) * E + e0 + 4 * lg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (e0 + 4 * lg + i < E)
+                dst[i] = acc[i];
+    }
+}
+
 // Tokens whose top-k one route workgroup takes: 16 when it is the only one,
 // else 4 (one wave per SIMD: the selection is a chain of wave reductions).
 constexpr int route_tpw(int T) { return T <= 16 ? 16 : 4; }
@@ -298,6 +346,17 @@ int router_small_rw(int E, int H, int act)
     if (act != ACT_BF16 || E % 16 != 0)
         return 0;
     return H % 256 == 0 ? 8 : H % 128 == 0 ? 4 : 0;
+}
+
+bool router_split_ok(int T, int E, int H, int act)
+{
+    return T >= 1 && T <= 16 && router_small_rw(E, H, act) == 8;
+}
+
+void launch_router_split(const RouterArgs &r, hipStream_t st)
+{
+    router_split<<<dim3(r.E / 16, 8), 64, 0, st>>>((const uint16_t *)r.x, (const uint16_t *)r.wr,
+                                                  r.logits, r.T, r.H, r.E);
 }
 
 void launch_router_small(const RouterArgs &r, hipStream_t st)
