@@ -627,6 +627,8 @@ def main():
     ap.add_argument("--no-small-sweep", action="store_true",
                     help="skip the small-T sweep of the MXFP4 layer")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the ceiling probes")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip sampling the clocks with rocm-smi (e.g. under a profiler)")
     ap.add_argument("--stack", type=int, default=16, metavar="L",
                     help="layers of the decode stack timed eager and as one HIP graph (0: skip)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -664,7 +666,7 @@ def main():
             for _ in range(10):
                 wl.step()
             torch.cuda.synchronize()
-    clocks = clock_log(busy)
+    clocks = None if args.no_clocks else clock_log(busy)
     d = describe(wl, wall, stages, steps, gwall)
     ms_step = wall / steps * 1e3
     out = {
