@@ -76,7 +76,7 @@ bool router_xq_ok(int E, int H, int act);
 size_t router_xq_bytes(int T, int H);
 void launch_router_small(const RouterArgs &r, hipStream_t st);  // logits only
 // Decode rows: the eight K-segment partial sums of router_small's logits as
-// planes [8][T][E] at r.logits (no bias), for the decode gate+up kernel to
+// [T][E][8] floats at r.logits (no bias), for the decode gate+up kernel to
 // add (T <= 16, bf16, router_small with 8 waves applicable).
 bool router_split_ok(int T, int E, int H, int act);
 void launch_router_split(const RouterArgs &r, hipStream_t st);

@@ -355,7 +355,7 @@ __global__ __launch_bounds__(64 * NW, WF ? 2 : 3) void expert_mxfp4(MxP p, const
 struct MxPairP {
     const uint16_t *x;            // [T, H]
     const uint8_t *xq;            // x quantised once per token (mxfp8.h records), or null
-    const float *logits;          // [T, E], or with nparts 8 the router's planes [8][T, E]
+    const float *logits;          // [T, E], or with nparts 8 the router's parts [T, E, 8]
     const float *bias;            // [E] or null: added here when nparts is 8
     const uint8_t *c0, *c1;       // gate / up codes, packed
     const uint8_t *s0, *s1;       // their scales, packed
@@ -379,26 +379,30 @@ __global__ __launch_bounds__(64 * NW, (WF && !PRE) ? 2 : 3) void expert_mxfp4_pa
     uint8_t *ahi = smem, *alo = ahi + ld, *shi = alo + ld, *slo = shi + nblk;
 
     // The token's logits and its activation row, requested together.  From
-    // the split router's eight partial-sum planes the logit is their sum in
-    // plane order plus the bias, as router_small forms it.
+    // the split router's eight partial sums (32 contiguous bytes per logit)
+    // the logit is their sum in segment order plus the bias, as router_small
+    // forms it.
     float v[PER];
     if (p.nparts == 8) {
-        const int64_t plane = (int64_t)p.T * p.E;
-        float q[8][PER];
+        float4 q[PER][2];
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-#pragma unroll
-            for (int i = 0; i < PER; ++i)
-                q[s][i] = lane + 64 * i < p.E
-                              ? p.logits[s * plane + (int64_t)t * p.E + lane + 64 * i]
-                              : 0.0f;
+        for (int i = 0; i < PER; ++i) {
+            const int e = min(lane + 64 * i, p.E - 1);
+            const float4 *src = (const float4 *)(p.logits + ((int64_t)t * p.E + e) * 8);
+            q[i][0] = src[0];
+            q[i][1] = src[1];
+        }
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int e = lane + 64 * i;
-            float a = q[0][i];
-#pragma unroll
-            for (int s = 1; s < 8; ++s)
-                a += q[s][i];
+            float a = q[i][0].x;
+            a += q[i][0].y;
+            a += q[i][0].z;
+            a += q[i][0].w;
+            a += q[i][1].x;
+            a += q[i][1].y;
+            a += q[i][1].z;
+            a += q[i][1].w;
             v[i] = e < p.E ? a + (p.bias ? p.bias[e] : 0.0f) : 0.0f;
         }
     } else {

@@ -111,9 +111,10 @@ __global__ __launch_bounds__(64 * RW) void router_small(const uint16_t *__restri
 // Decode rows (T <= 16: one token block): router_small's eight K-segment
 // waves as eight workgroups of one wave each, so that the router matrix is
 // read by eight times as many CUs.  Segment `seg` of expert block
-// blockIdx.x writes its partial sums to part[seg][t][e]; the decode gate+up
-// kernel adds the eight in segment order and then the bias, which is the
-// sum router_small forms in LDS (so the logits have the same bits).
+// blockIdx.x writes its partial sums to part[t][e][seg] (a logit's eight
+// parts in 32 contiguous bytes); the decode gate+up kernel adds the eight in
+// segment order and then the bias, which is the sum router_small forms in
+// LDS (so the logits have the same bits).
 __global__ __launch_bounds__(64) void router_split(const uint16_t *__restrict__ x,
                                                    const uint16_t *__restrict__ wr,
                                                    float *__restrict__ part, int T, int H, int E)
@@ -148,11 +149,11 @@ __global__ __launch_bounds__(64) void router_split(const uint16_t *__restrict__ 
     }
     // C[expert 4*lg + i][token l16]
     if (l16 < T) {
-        float *dst = part + ((int64_t)seg * T + l16) * E + e0 + 4 * lg;
+        float *dst = part + ((int64_t)l16 * E + e0 + 4 * lg) * 8 + seg;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (e0 + 4 * lg + i < E)
-                dst[i] = acc[i];
+                dst[8 * i] = acc[i];
     }
 }
 
