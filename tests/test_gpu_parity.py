@@ -274,6 +274,37 @@ def test_mxfp4_decode_sizes(T):
     check_err("mxfp4 decode T=%d" % T, hx.rel_err(hx.y_host(y, c["act"]), y_ref), "mxfp4")
 
 
+@pytest.mark.parametrize("T,bias", [(1, None), (6, None), (8, "zipf1.1"), (1, "zipf1.1")])
+def test_decode_routing_matches_the_route_export(T, bias):
+    """MXFP4 decode rows take their logits from the split router and select
+    inside the gate+up kernel; moe_route takes them from router_small and
+    selects in route_small.  Both must give the same indices and weights bit
+    for bit (the same logit arithmetic and the same wave selection), with and
+    without a router bias (which the decode gate+up kernel adds itself), and
+    y must match the oracle."""
+    say("[decode routing] T =", T, "bias", bias)
+    c0, g = layer("c4_t6")
+    c = dict(c0, T=T, seed=5100 + T, bias=bias)
+    lay = g.lay
+    if bias is not None:
+        lay = mi.LayerData(c=c, router_w=lay.router_w, router_bias=mi.router_bias(c),
+                           w_gate=lay.w_gate, w_up=lay.w_up, w_down=lay.w_down,
+                           s_gate=lay.s_gate, s_up=lay.s_up, s_down=lay.s_down)
+    gl = hx.GpuLayer(c, lay)
+    x = hx.margin_x(c, lay)
+    xd = hx.act_torch(x, c["act"], "cuda")
+    y, idx, w = gl.forward(xd)
+    idx2, w2, _, _, _ = gl.route(xd)
+    assert torch.equal(idx.cpu(), idx2.cpu())
+    assert torch.equal(w.cpu().view(torch.int32), w2.cpu().view(torch.int32))
+    idx_r, _, _ = oracle.route(hx.router_only_layer(c, lay), x)
+    assert np.array_equal(idx.cpu().numpy(), idx_r)
+    experts = sorted(set(idx_r.reshape(-1).tolist()))
+    y_ref, _, _ = oracle.forward(hx.oracle_layer(c, lay, experts), x, np.arange(T, dtype=np.int32))
+    check_err("mxfp4 decode T=%d bias %s" % (T, bias), hx.rel_err(hx.y_host(y, c["act"]), y_ref),
+              "mxfp4")
+
+
 def _dequantised_bf16_layer(c, lay, experts):
     """A bf16 layer holding exactly the values the MXFP4 layer decodes to
     (E2M1 code x 2^(s-127) has at most two significant bits, so bf16 holds
