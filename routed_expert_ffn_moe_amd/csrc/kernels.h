@@ -17,6 +17,7 @@ struct RouterArgs {
     const void *x;        // [T, H] act
     const void *wr;       // [E, H] act
     const float *bias;    // [E] or null
+    int nparts;           // 8: logits holds the split router's parts [T][E][8] (route_small)
     float *logits;        // [T, E] workspace
     int32_t *idx;         // [T, k]
     float *w;             // [T, k]
@@ -75,9 +76,10 @@ int router_small_rw(int E, int H, int act);  // waves of router_small, 0 if it d
 bool router_xq_ok(int E, int H, int act);
 size_t router_xq_bytes(int T, int H);
 void launch_router_small(const RouterArgs &r, hipStream_t st);  // logits only
-// Decode rows: the eight K-segment partial sums of router_small's logits as
-// [T][E][8] floats at r.logits (no bias), for the decode gate+up kernel to
-// add (T <= 16, bf16, router_small with 8 waves applicable).
+// Short passes: the eight K-segment partial sums of router_small's logits as
+// [T][E][8] floats at r.logits (no bias), for the decode gate+up kernel or
+// route_small to add (T <= 64, bf16, router_small with 8 waves applicable);
+// clears r.ticket (if given) as router_small does.
 bool router_split_ok(int T, int E, int H, int act);
 void launch_router_split(const RouterArgs &r, hipStream_t st);
 void launch_route_small(const RouterArgs &r, const PermuteArgs &a, hipStream_t st);  // top-k + permutation

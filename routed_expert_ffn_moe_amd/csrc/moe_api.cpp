@@ -313,9 +313,16 @@ int route_pass(const moe_shape_t *s, const moe_weights_t *w, const void *x, int 
     const bool seg = !small && moe::router_parts(Tc, s->H, s->E, r.act) == 8;
     r.hist = seg ? (int32_t *)(ws + L.blk) : nullptr;
     r.nhist = moe::permute_blocks(Tc * s->top_k) * s->E;
+    // passes of up to 64 tokens: the split router, whose partial sums
+    // route_small adds
+    const bool split = small && !r.xq && moe::router_split_ok(Tc, s->E, s->H, r.act) &&
+                       (int64_t)8 * Tc * s->E <= L.logit_floats;
+    r.nparts = split ? 8 : 1;
     {
         StageScope sc(0, st);
-        if (small)
+        if (split)
+            moe::launch_router_split(r, st);
+        else if (small)
             moe::launch_router_small(r, st);  // top-k moves into the permutation pass
         else
             moe::launch_router(r, st);

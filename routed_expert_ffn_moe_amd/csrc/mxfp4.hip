@@ -384,27 +384,7 @@ __global__ __launch_bounds__(64 * NW, (WF && !PRE) ? 2 : 3) void expert_mxfp4_pa
     // forms it.
     float v[PER];
     if (p.nparts == 8) {
-        float4 q[PER][2];
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int e = min(lane + 64 * i, p.E - 1);
-            const float4 *src = (const float4 *)(p.logits + ((int64_t)t * p.E + e) * 8);
-            q[i][0] = src[0];
-            q[i][1] = src[1];
-        }
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int e = lane + 64 * i;
-            float a = q[i][0].x;
-            a += q[i][0].y;
-            a += q[i][0].z;
-            a += q[i][0].w;
-            a += q[i][1].x;
-            a += q[i][1].y;
-            a += q[i][1].z;
-            a += q[i][1].w;
-            v[i] = e < p.E ? a + (p.bias ? p.bias[e] : 0.0f) : 0.0f;
-        }
+        wave_logits_from_parts<PER>(p.logits, p.bias, t, p.E, v);
     } else {
 #pragma unroll
         for (int i = 0; i < PER; ++i)

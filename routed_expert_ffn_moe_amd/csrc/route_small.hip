@@ -108,22 +108,27 @@ __global__ __launch_bounds__(64 * RW) void router_small(const uint16_t *__restri
     }
 }
 
-// Decode rows (T <= 16: one token block): router_small's eight K-segment
-// waves as eight workgroups of one wave each, so that the router matrix is
-// read by eight times as many CUs.  Segment `seg` of expert block
-// blockIdx.x writes its partial sums to part[t][e][seg] (a logit's eight
+// Short passes (T <= 64): router_small's eight K-segment waves as eight
+// workgroups of one wave each, so that the router matrix is read by eight
+// times as many CUs.  Segment `seg` (blockIdx.y) of expert block blockIdx.x
+// and token block blockIdx.z writes its partial sums to part[t][e][seg] (a
+// logit's eight
 // parts in 32 contiguous bytes); the decode gate+up kernel adds the eight in
 // segment order and then the bias, which is the sum router_small forms in
 // LDS (so the logits have the same bits).
 __global__ __launch_bounds__(64) void router_split(const uint16_t *__restrict__ x,
                                                    const uint16_t *__restrict__ wr,
-                                                   float *__restrict__ part, int T, int H, int E)
+                                                   float *__restrict__ part,
+                                                   int32_t *__restrict__ ticket, int T, int H,
+                                                   int E)
 {
     const int lane = threadIdx.x, l16 = lane & 15, lg = lane >> 4;
-    const int e0 = blockIdx.x * 16, seg = blockIdx.y;
+    const int e0 = blockIdx.x * 16, seg = blockIdx.y, t = blockIdx.z * 16 + l16;
+    if (ticket && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && lane == 0)
+        *ticket = 0;  // the route kernel after this one counts on it
     const int kq = H / 8;  // K share of this segment (multiple of 32)
     const uint16_t *wp = wr + (int64_t)min(e0 + l16, E - 1) * H + seg * kq + lg * 8;
-    const uint16_t *xp = x + (int64_t)min(l16, T - 1) * H + seg * kq + lg * 8;
+    const uint16_t *xp = x + (int64_t)min(t, T - 1) * H + seg * kq + lg * 8;
     const int nst = kq / 32;
     uint4 wq[RS_RING], xq[RS_RING];
 #pragma unroll
@@ -147,9 +152,9 @@ __global__ __launch_bounds__(64) void router_split(const uint16_t *__restrict__ 
             }
         }
     }
-    // C[expert 4*lg + i][token l16]
-    if (l16 < T) {
-        float *dst = part + ((int64_t)l16 * E + e0 + 4 * lg) * 8 + seg;
+    // C[expert 4*lg + i][token l16 of the block]
+    if (t < T) {
+        float *dst = part + ((int64_t)t * E + e0 + 4 * lg) * 8 + seg;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (e0 + 4 * lg + i < E)
@@ -163,7 +168,8 @@ constexpr int route_tpw(int T) { return T <= 16 ? 16 : 4; }
 
 template <int PER>
 __global__ __launch_bounds__(1024) void route_small(
-    const float *__restrict__ logits, int32_t *__restrict__ idx, float *__restrict__ w, int T,
+    const float *__restrict__ logits, const float *__restrict__ bias, int nparts,
+    int32_t *__restrict__ idx, float *__restrict__ w, int T,
     int E, int k, int shared, int32_t *__restrict__ ticket, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ row_src, int32_t *__restrict__ row_tok,
     int32_t *__restrict__ row_of, Tile *__restrict__ tiles_a, int32_t *__restrict__ ntiles_a,
@@ -186,9 +192,17 @@ __global__ __launch_bounds__(1024) void route_small(
     // 1. top-k and weights of this workgroup's tokens, one wave per token
     const int tpw = route_tpw(T);
     const int t = blockIdx.x * tpw + wv;
-    if (wv < tpw && t < T)
-        wave_topk<PER>(logits + (int64_t)t * E, E, k, idx + (int64_t)t * k, w + (int64_t)t * k,
-                       one ? s_idx + t * k : nullptr);
+    if (wv < tpw && t < T) {
+        if (nparts == 8) {  // the split router's partial sums
+            float v[PER];
+            wave_logits_from_parts<PER>(logits, bias, t, E, v);
+            wave_topk_vals<PER>(v, E, k, idx + (int64_t)t * k, w + (int64_t)t * k,
+                                one ? s_idx + t * k : nullptr);
+        } else {
+            wave_topk<PER>(logits + (int64_t)t * E, E, k, idx + (int64_t)t * k,
+                           w + (int64_t)t * k, one ? s_idx + t * k : nullptr);
+        }
+    }
     if (!one) {
         // The last workgroup through here does the rest.  The barrier orders
         // the workgroup's stores before thread 0's device-scope release, which
@@ -351,13 +365,13 @@ int router_small_rw(int E, int H, int act)
 
 bool router_split_ok(int T, int E, int H, int act)
 {
-    return T >= 1 && T <= 16 && router_small_rw(E, H, act) == 8;
+    return T >= 1 && T <= 64 && router_small_rw(E, H, act) == 8;
 }
 
 void launch_router_split(const RouterArgs &r, hipStream_t st)
 {
-    router_split<<<dim3(r.E / 16, 8), 64, 0, st>>>((const uint16_t *)r.x, (const uint16_t *)r.wr,
-                                                  r.logits, r.T, r.H, r.E);
+    router_split<<<dim3(r.E / 16, 8, (r.T + 15) / 16), 64, 0, st>>>(
+        (const uint16_t *)r.x, (const uint16_t *)r.wr, r.logits, r.ticket, r.T, r.H, r.E);
 }
 
 void launch_router_small(const RouterArgs &r, hipStream_t st)
@@ -383,7 +397,8 @@ static void route_small_per(const RouterArgs &r, const PermuteArgs &a, hipStream
 {
     const int tpw = route_tpw(r.T);
     route_small<PER><<<(r.T + tpw - 1) / tpw, 1024, 0, st>>>(
-        r.logits, r.idx, r.w, r.T, r.E, r.k, a.shared, r.ticket, a.counts, a.offsets, a.row_src,
+        r.logits, r.bias, r.nparts, r.idx, r.w, r.T, r.E, r.k, a.shared, r.ticket, a.counts,
+        a.offsets, a.row_src,
         a.row_tok, a.row_of, a.tiles_a, a.ntiles_a, a.tiles_b, a.ntiles_b, a.bm_a, a.bm_b,
         a.items_a, a.ntn_a, a.wrows_a, a.items_b, a.ntn_b, a.wrows_b);
 }

@@ -159,6 +159,39 @@ __device__ __forceinline__ void wave_topk(const float *__restrict__ lrow, int E,
     wave_topk_vals<PER>(v, E, k, idx, w, sidx);
 }
 
+// Token t's logits (lane l: experts l, l+64, ...) from the split router's
+// eight partial sums per logit (32 contiguous bytes, [T][E][8]): their sum
+// in segment order, then the bias - the arithmetic of router_small.  Slots
+// past E hold 0.
+template <int PER>
+__device__ __forceinline__ void wave_logits_from_parts(const float *__restrict__ parts,
+                                                       const float *__restrict__ bias, int t,
+                                                       int E, float (&v)[PER])
+{
+    const int lane = threadIdx.x & 63;
+    float4 q[PER][2];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = min(lane + 64 * i, E - 1);
+        const float4 *src = (const float4 *)(parts + ((int64_t)t * E + e) * 8);
+        q[i][0] = src[0];
+        q[i][1] = src[1];
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = lane + 64 * i;
+        float a = q[i][0].x;
+        a += q[i][0].y;
+        a += q[i][0].z;
+        a += q[i][0].w;
+        a += q[i][1].x;
+        a += q[i][1].y;
+        a += q[i][1].z;
+        a += q[i][1].w;
+        v[i] = e < E ? a + (bias ? bias[e] : 0.0f) : 0.0f;
+    }
+}
+
 // Logit slots per lane for E experts: 1, 2, 4, 8 or 16.
 inline int topk_per(int E)
 {
