@@ -137,13 +137,17 @@ def layer_roofline(work, ms_step, dtype):
             "measured_us": round(ms_step * 1e3, 2), "frac": round(t_roof / (ms_step / 1e3), 4)}
 
 
-def weight_sets(c):
+def weight_sets(c, touched=None):
     """Independent weight sets to rotate through so that consecutive calls
     find their expert weights in HBM, not in the 256 MB infinity cache: one
     when a call touches more than twice that, else enough sets (at most 16)
-    to exceed it twice over."""
-    per_call = min(c["top_k"] * c["T"], c["E"]) * 3 * c["H"] * c["I"] * (
-        17.0 / 32.0 if c["w"] == "mxfp4" else 2)
+    to exceed it twice over.  `touched` is the number of experts one call
+    routes to; without it every pair is taken to pick a distinct expert,
+    which a skewed router bias makes far too many (Zipf(1.1) at T=16 reaches
+    about a third of them)."""
+    if touched is None:
+        touched = min(c["top_k"] * c["T"], c["E"])
+    per_call = touched * 3 * c["H"] * c["I"] * (17.0 / 32.0 if c["w"] == "mxfp4" else 2)
     return 1 if per_call > 2 * MALL_BYTES else int(min(16, 2 * MALL_BYTES // max(per_call, 1) + 1))
 
 
@@ -158,38 +162,11 @@ class Workload:
         self.keep_rowmajor = keep_rowmajor
         self.c = dict(cfg) if cfg is not None else mi.cfg(name)
         c = self.c
-        if wsets is None:
-            wsets = weight_sets(c)
-        self.layers = [mi.make_layer(c, dev, s) for s in range(wsets)]
+        self.mi, self.dev = mi, dev
         x = mi.make_x(c)
         self.x_host = x
         t = torch.from_numpy(x)
         self.x = (t.view(torch.int16).view(torch.bfloat16) if c["act"] == "bf16" else t).to(dev)
-        self.weights = []
-        self._keep = []
-        for lay in self.layers:
-            rw = torch.from_numpy(lay.router_w)
-            rw = (rw.view(torch.int16).view(torch.bfloat16) if c["act"] == "bf16" else rw).to(dev)
-            rb = None if lay.router_bias is None else torch.from_numpy(lay.router_bias).to(dev)
-            self._keep += [rw, rb]
-            wg, wu, wd = lay.w_gate, lay.w_up, lay.w_down
-            sg, su, sd = lay.s_gate, lay.s_up, lay.s_down
-            shg, shu, shd = lay.sh_gate, lay.sh_up, lay.sh_down
-            # one-time repack into the layouts the kernels read (the row-major
-            # copies go, so that the widest layer still fits twice over)
-            if c["w"] == "mxfp4":
-                (wg, sg), (wu, su), (wd, sd) = (moe.pack_mxfp4(wg, sg), moe.pack_mxfp4(wu, su),
-                                                moe.pack_mxfp4(wd, sd))
-            elif c["w"] == "bf16":
-                wg, wu, wd = (self._packed(lay, "w_gate"), self._packed(lay, "w_up"),
-                              self._packed(lay, "w_down"))
-            if c["act"] == "bf16" and shg is not None:
-                shg, shu, shd = (self._packed(lay, "sh_gate"), self._packed(lay, "sh_up"),
-                                 self._packed(lay, "sh_down"))
-            self._keep += [wg, wu, wd, sg, su, sd, shg, shu, shd]
-            self.weights.append(moe.make_weights(rw, wg, wu, wd, router_bias=rb, s_gate=sg,
-                                                 s_up=su, s_down=sd, sh_gate=shg,
-                                                 sh_up=shu, sh_down=shd))
         self.shape = moe.make_shape(c["T"], c["H"], c["E"], c["top_k"], c["I"], c["I_shared"],
                                     0, c["act"], c["w"])
         nb = moe.moe_workspace_bytes(self.shape)
@@ -198,6 +175,44 @@ class Workload:
         self.idx = torch.empty((c["T"], c["top_k"]), dtype=torch.int32, device=dev)
         self.w = torch.empty((c["T"], c["top_k"]), dtype=torch.float32, device=dev)
         self.i = 0
+        self.layers, self.weights, self._keep = [], [], []
+        self._add_set(0)
+        if wsets is None:
+            # one routed call on the first set counts the experts a call touches
+            self.step()
+            self.i = 0
+            wsets = weight_sets(c, int((self.counts() > 0).sum()))
+        for s in range(1, wsets):
+            self._add_set(s)
+
+    def _add_set(self, s):
+        """Draws weight set s, packs it and appends it to the rotation."""
+        torch, moe, c = self.torch, self.moe, self.c
+        lay = self.mi.make_layer(c, self.dev, s)
+        self.layers.append(lay)
+        dev = self.dev
+        rw = torch.from_numpy(lay.router_w)
+        rw = (rw.view(torch.int16).view(torch.bfloat16) if c["act"] == "bf16" else rw).to(dev)
+        rb = None if lay.router_bias is None else torch.from_numpy(lay.router_bias).to(dev)
+        self._keep += [rw, rb]
+        wg, wu, wd = lay.w_gate, lay.w_up, lay.w_down
+        sg, su, sd = lay.s_gate, lay.s_up, lay.s_down
+        shg, shu, shd = lay.sh_gate, lay.sh_up, lay.sh_down
+        # one-time repack into the layouts the kernels read (the row-major
+        # copies go, so that the widest layer still fits twice over)
+        if c["w"] == "mxfp4":
+            (wg, sg), (wu, su), (wd, sd) = (moe.pack_mxfp4(wg, sg), moe.pack_mxfp4(wu, su),
+                                            moe.pack_mxfp4(wd, sd))
+        elif c["w"] == "bf16":
+            wg, wu, wd = (self._packed(lay, "w_gate"), self._packed(lay, "w_up"),
+                          self._packed(lay, "w_down"))
+        if c["act"] == "bf16" and shg is not None:
+            shg, shu, shd = (self._packed(lay, "sh_gate"), self._packed(lay, "sh_up"),
+                             self._packed(lay, "sh_down"))
+        self._keep += [wg, wu, wd, sg, su, sd, shg, shu, shd]
+        self.weights.append(moe.make_weights(rw, wg, wu, wd, router_bias=rb, s_gate=sg,
+                                             s_up=su, s_down=sd, sh_gate=shg,
+                                             sh_up=shu, sh_down=shd))
 
     def step(self):
         wt = self.weights[self.i % len(self.weights)]

@@ -89,6 +89,19 @@ def test_weight_sets_exceed_the_infinity_cache():
     assert bench.weight_sets(mi.cfg("c3")) == 1
 
 
+def test_weight_sets_follow_the_touched_experts():
+    """With the experts a call actually touches, a skewed router that keeps
+    to a few experts gets the rotation its own bytes need: 40 MXFP4 experts
+    of H=2048, I=768 are 100 MB per call, so six sets pass 512 MB."""
+    c = mi.cfg("c4_p2048", T=16)
+    per = 3 * c["H"] * c["I"] * 17 / 32
+    assert bench.weight_sets(c) == 2           # 128 distinct experts assumed
+    n = bench.weight_sets(c, touched=40)
+    assert n == 6 and n * 40 * per > 2 * bench.MALL_BYTES
+    assert bench.weight_sets(c, touched=1) == 16
+    assert bench.weight_sets(mi.cfg("c2"), touched=200) == 1
+
+
 def test_traffic_records_only_for_the_current_sources(tmp_path, monkeypatch):
     sha = bench.kernel_sources_sha1()
     (tmp_path / "hbm_traffic_counters.md").write_text(
