@@ -1,7 +1,8 @@
 """The C ABI without a GPU: the library loads, exports every function that
 include/moe.h declares, sizes workspaces, and rejects bad arguments with the
 documented codes before touching any device (every case below carries at
-least one argument error, so no kernel is ever launched)."""
+least one argument error, so no kernel is ever launched, except the one
+valid call, which runs only where the machine has no GPU driver at all)."""
 import ctypes
 import os
 import re
@@ -170,6 +171,18 @@ def test_route_rejects_chunking():
 
 def test_zero_tokens_returns_ok_without_touching_buffers():
     assert call(shape(T=0), x=0, y=0, idx=0, ws=0) == moe.MOE_OK
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                    reason="a GPU driver is present: a valid call would launch on fake addresses")
+def test_valid_call_without_a_device_fails_loudly():
+    """Every argument is valid, so the call reaches the device check, which
+    finds no HIP device: an error code and a message, never a CPU path."""
+    sh = shape()
+    nb = moe.moe_workspace_bytes(sh)
+    lib = moe.load()
+    assert call(sh, ws_bytes=nb) == moe.MOE_EHIP
+    assert b"hipGetDevice" in lib.moe_last_error()
 
 
 @pytest.mark.parametrize("E,N,K,ptrs", [
