@@ -61,7 +61,7 @@ CONFIGS: Dict[str, dict] = {
 LAYER_SEED = {"L0": 100, "L1": 101, "L3": 103, "L4": 104,
               # small layers of other shapes (the tests' sweep of kernel variants)
               "SA": 201, "SB": 202, "SC": 203, "SD": 204, "SE": 205, "SF": 206, "SG": 207,
-              "SH": 208, "SI": 209}
+              "SH": 208, "SI": 209, "SJ": 210, "SK": 211}
 W_STD = 0.02      # std of router and expert weights
 MARGIN = 1e-3     # minimum top-k logit gap of accepted token rows
 

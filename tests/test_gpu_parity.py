@@ -486,6 +486,11 @@ SWEEP = {
                bias="zipf1.1"),
     "SI": dict(T=640, H=1024, E=8, top_k=2, I=512, I_shared=512, act="bf16", w="bf16",
                bias="uniform"),
+    # MXFP4 decode rows of a narrower layer (H=1024, I=512, at most 64
+    # experts: one 64-lane word of logits per token), several rows and one
+    "SJ": dict(T=5, H=1024, E=64, top_k=6, I=512, I_shared=0, act="bf16", w="mxfp4",
+               bias="zipf1.1"),
+    "SK": dict(T=1, H=1024, E=48, top_k=4, I=512, I_shared=0, act="bf16", w="mxfp4", bias=None),
 }
 
 
