@@ -90,11 +90,28 @@ __device__ __forceinline__ uint4 wload(const uint16_t *p)
 }
 
 template <int N>
-__device__ __forceinline__ void chunk_store(const u32v<N> &r, uint16_t *dst, const int (&off)[N])
+__device__ __forceinline__ void chunk_store(const u32v<N> &r, uint16_t *dst, const int (&off)[N],
+                                            int part = 0, int nparts = 1)
 {
 #pragma unroll
     for (int i = 0; i < N; ++i)
-        *(uint4 *)(dst + off[i]) = uint4{r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]};
+        if (i % nparts == part)
+            *(uint4 *)(dst + off[i]) = uint4{r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]};
+}
+
+// The next token chunk goes to LDS (the other buffer, free since the last
+// barrier) during a chunk's MFMAs: the even pieces after the first K step,
+// the odd ones after the third (the last, for shorter chunks), instead of
+// all after the chunk, where the matrix cores waited for the LDS writes
+// (T=2048 MXFP4 gate+up 185.6 -> 181.3 us, the bf16 layers -0.5%, the same
+// results bit for bit).  Returns the part written after step st, or -1.
+template <int SPC>
+__device__ __forceinline__ int store_part(int st)
+{
+    static_assert(SPC >= 2, "both parts of the chunk are written");
+    if (st == 0)
+        return 0;
+    return st == (SPC > 2 ? 2 : SPC - 1) ? 1 : -1;
 }
 
 // One work item: up to BM rows of one expert (group g) and a 128-row slice
@@ -158,7 +175,7 @@ __device__ __forceinline__ void frag_load(bf16x8 (&tf)[NMB], const uint16_t *As,
 // The SKC/32 K steps of a staged token chunk.  Step s consumes the weight
 // fragments of ring slot (slot0 + s) % SD and refills it from the step SD
 // ahead (chunk wl[(s + SD) / SPC], step (s + SD) % SPC); the token fragments
-// of step s + 1 are read from LDS before the MFMAs of step s run, so LDS
+// of step s + 1 are read from LDS while the MFMAs of step s run, so LDS
 // latency hides behind them.
 // With `full` false (uniform) only the first half of the MB token blocks is
 // read and multiplied: the rest of the item's row tile is empty.
@@ -174,11 +191,12 @@ __device__ __forceinline__ void mac(floatx4 &c, bf16x8 a, bf16x8 b)
         c = mfma16(a, b, c);
 }
 
-template <int MB, int NB, int CB, int SD, int SKC, bool AGPR>
+template <int MB, int NB, int CB, int SD, int SKC, bool AGPR, class Store>
 __device__ __forceinline__ void kchunk(bool full, const uint16_t *As, int slot0, int l16, int lg,
                                        uint4 (&bq)[SD][NB][CB],
                                        const uint16_t *const (&wl)[3][NB],
-                                       const int (&woff)[CB], floatx4 (&acc)[NB][CB][MB])
+                                       const int (&woff)[CB], floatx4 (&acc)[NB][CB][MB],
+                                       const Store &store)
 {
     constexpr int SPC = SKC / 32, SLD = sld_of(SKC);
     static_assert((SPC - 1 + SD) / SPC <= 2, "refills reach at most two chunks ahead");
@@ -197,18 +215,29 @@ __device__ __forceinline__ void kchunk(bool full, const uint16_t *As, int slot0,
                 wf[m][cb] = as_bf16x8(bq[slot][m][cb]);
                 bq[slot][m][cb] = wload<(MB <= 2)>(w[m] + woff[cb] + wk * 32);
             }
-        if (st + 1 < SPC)
+        // The next step's token fragments are read after the MFMAs of this
+        // step's second token block (before the MFMAs when the first half
+        // holds fewer than two blocks).  Read before all of them, they were
+        // waited for together with this step's own: the LDS wait counter
+        // holds 15 operations and a step reads 8, so the compiler drained
+        // both steps' reads before the first MFMA (T=2048 gate+up 172 ->
+        // 170 us, the same results bit for bit).
+        constexpr int AT = MB / 2 >= 2 ? 1 : MB / 2 - 1;
+        if (AT < 0 && st + 1 < SPC)
             frag_load<MB, SLD>(tf[(st + 1) & 1], As, st + 1, l16, lg, full);
-        // issue the refills and the next fragments here, not later: the
-        // waits for this step's operands must not have to wait for them
+        // issue the refills here, not later: the waits for this step's
+        // operands must not have to wait for them
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mb = 0; mb < MB / 2; ++mb)
+        for (int mb = 0; mb < MB / 2; ++mb) {
 #pragma unroll
             for (int m = 0; m < NB; ++m)
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb)
                     mac<AGPR>(acc[m][cb][mb], wf[m][cb], tf[st & 1][mb]);
+            if (mb == AT && st + 1 < SPC)
+                frag_load<MB, SLD>(tf[(st + 1) & 1], As, st + 1, l16, lg, full);
+        }
         if (full || MB < 2) {
 #pragma unroll
             for (int mb = MB / 2; mb < MB; ++mb)
@@ -218,6 +247,8 @@ __device__ __forceinline__ void kchunk(bool full, const uint16_t *As, int slot0,
                     for (int cb = 0; cb < CB; ++cb)
                         mac<AGPR>(acc[m][cb][mb], wf[m][cb], tf[st & 1][mb]);
         }
+        if (store_part<SPC>(st) >= 0)
+            store(store_part<SPC>(st));
     }
 }
 
@@ -227,11 +258,12 @@ __device__ __forceinline__ void kchunk(bool full, const uint16_t *As, int slot0,
 // after its last MFMA: the ring then needs no second copy of the fragments
 // in use, for which the 256 accumulators of a wide tile leave no registers.
 // A refill still lands SD steps ahead of its use.
-template <int NMB, int MB, int NB, int CB, int SD, int SKC>
+template <int NMB, int MB, int NB, int CB, int SD, int SKC, class Store>
 __device__ __forceinline__ void kchunk_wide(const uint16_t *As, int slot0, int l16, int lg,
                                             uint4 (&bq)[SD][NB][CB],
                                             const uint16_t *const (&wl)[3][NB],
-                                            const int (&woff)[CB], floatx4 (&acc)[NB][CB][MB])
+                                            const int (&woff)[CB], floatx4 (&acc)[NB][CB][MB],
+                                            const Store &store)
 {
     constexpr int SPC = SKC / 32, SLD = sld_of(SKC);
     static_assert((SPC - 1 + SD) / SPC <= 2, "refills reach at most two chunks ahead");
@@ -242,8 +274,6 @@ __device__ __forceinline__ void kchunk_wide(const uint16_t *As, int slot0, int l
         const int slot = (slot0 + st) % SD;
         const uint16_t *const *w = wl[(st + SD) / SPC];
         const int wk = ((st + SD) % SPC) * 32;
-        if (st + 1 < SPC)
-            frag_load<NMB, SLD>(tf[(st + 1) & 1], As, st + 1, l16, lg, true);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int m = 0; m < NB; ++m)
@@ -254,8 +284,14 @@ __device__ __forceinline__ void kchunk_wide(const uint16_t *As, int slot0, int l
                 for (int mb = 0; mb < NMB; ++mb)
                     mfma16_acc(acc[m][cb][mb], wf, tf[st & 1][mb]);
                 bq[slot][m][cb] = wload<false>(w[m] + woff[cb] + wk * 32);
+                // the next step's fragments once the first fragment's MFMAs
+                // have taken all of this step's (see kchunk)
+                if (m == 0 && cb == 0 && st + 1 < SPC)
+                    frag_load<NMB, SLD>(tf[(st + 1) & 1], As, st + 1, l16, lg, true);
                 __builtin_amdgcn_sched_barrier(0);
             }
+        if (store_part<SPC>(st) >= 0)
+            store(store_part<SPC>(st));
     }
 }
 
@@ -294,12 +330,13 @@ __device__ __forceinline__ void frag_load_w4(bf16x8 (&tf)[NMB], const uint16_t *
 // ahead (codes at wl[m] + cb's block offset, scale bytes at sl[m]); the
 // token fragments of sub-step s + 1 are read from LDS before the MFMAs of
 // sub-step s.
-template <int MB, int NB, int CB, int SD, bool AGPR>
+template <int MB, int NB, int CB, int SD, bool AGPR, class Store>
 __device__ __forceinline__ void kchunk_w4(bool full, const uint16_t *As, int slot, int l16, int lg,
                                           uint4 (&bq)[SD][NB][CB], uint32_t (&sq)[SD][NB][CB],
                                           const uint8_t *const (&wl)[NB],
                                           const uint8_t *const (&sl)[NB], const int (&woff)[CB],
-                                          const int (&soff)[CB], floatx4 (&acc)[NB][CB][MB])
+                                          const int (&soff)[CB], floatx4 (&acc)[NB][CB][MB],
+                                          const Store &store)
 {
     constexpr int SLD = sld_of(128);
     uint4 wq[NB][CB];
@@ -318,7 +355,10 @@ __device__ __forceinline__ void kchunk_w4(bool full, const uint16_t *As, int slo
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-        if (st + 1 < 4)
+        // the next sub-step's fragments after the second token block's
+        // MFMAs, as in kchunk
+        constexpr int AT = MB / 2 >= 2 ? 1 : MB / 2 - 1;
+        if (AT < 0 && st + 1 < 4)
             frag_load_w4<MB, SLD>(tf[(st + 1) & 1], As, st + 1, l16, lg, full);
         bf16x8 wf[NB][CB];
 #pragma unroll
@@ -329,12 +369,15 @@ __device__ __forceinline__ void kchunk_w4(bool full, const uint16_t *As, int slo
                 wf[m][cb] = fp4x8_bf16(c4[st], ws[m][cb]);
             }
 #pragma unroll
-        for (int mb = 0; mb < MB / 2; ++mb)
+        for (int mb = 0; mb < MB / 2; ++mb) {
 #pragma unroll
             for (int m = 0; m < NB; ++m)
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb)
                     mac<AGPR>(acc[m][cb][mb], wf[m][cb], tf[st & 1][mb]);
+            if (mb == AT && st + 1 < 4)
+                frag_load_w4<MB, SLD>(tf[(st + 1) & 1], As, st + 1, l16, lg, full);
+        }
         if (full || MB < 2) {
 #pragma unroll
             for (int mb = MB / 2; mb < MB; ++mb)
@@ -344,6 +387,8 @@ __device__ __forceinline__ void kchunk_w4(bool full, const uint16_t *As, int slo
                     for (int cb = 0; cb < CB; ++cb)
                         mac<AGPR>(acc[m][cb][mb], wf[m][cb], tf[st & 1][mb]);
         }
+        if (store_part<4>(st) >= 0)
+            store(store_part<4>(st));
     }
 }
 
@@ -505,6 +550,12 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
             for (int h = 0; h < 2; ++h) {
                 const int cc = c + h;
                 const uint16_t *As = sA[buf];
+                // Token chunk pipeline: rt[h % TL] holds the chunk after this
+                // one; it goes to the other LDS buffer during this chunk's
+                // MFMAs and is reloaded with the chunk TL + 1 ahead.
+                u32v<ACH> &ra = rt[h % TL];
+                uint16_t *const Bn = sA[buf ^ 1];
+                const auto store = [&](int part) { chunk_store<ACH>(ra, Bn, aoff, part, 2); };
                 if (W4) {
                     // the chunk SD = 2 ahead refills this one's ring slot
                     const int t = cc + 2;
@@ -517,7 +568,7 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
                         sl4[m] = (over ? qn[m] : qc[m]) + tq;
                     }
                     kchunk_w4<MB, NB, CB, SD, AGPR>(full, As, h, l16, lg, bq, sq, wl4, sl4, woff,
-                                                    soff, acc);
+                                                    soff, acc, store);
                 } else {
                     // Weight chunks d = 0, 1, 2 after this one, from this item
                     // or (past its end) from the next one; branch-free on purpose.
@@ -538,15 +589,12 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
                     // instantiation for half-filled tiles costs their
                     // accumulators a round of copies at each branch)
                     if (WIDE)
-                        kchunk_wide<MB, MB, NB, CB, SD, SKC>(As, h * SPC, l16, lg, bq, wl, woff, acc);
+                        kchunk_wide<MB, MB, NB, CB, SD, SKC>(As, h * SPC, l16, lg, bq, wl, woff, acc,
+                                                             store);
                     else
                         kchunk<MB, NB, CB, SD, SKC, AGPR>(full, As, h * SPC, l16, lg, bq, wl, woff,
-                                                          acc);
+                                                          acc, store);
                 }
-                // Token chunk pipeline: rt[h % TL] holds the chunk after this
-                // one and is reloaded with the chunk TL + 1 ahead.
-                u32v<ACH> &ra = rt[h % TL];
-                chunk_store<ACH>(ra, sA[buf ^ 1], aoff);
                 __syncthreads();
                 buf ^= 1;
                 const int c2 = cc + 1 + TL;
