@@ -220,7 +220,20 @@ class Workload:
         self.moe.moe_forward(self.shape, wt, self.x, self.y, self.idx, self.w, self.ws)
 
     def time(self, steps, warmup):
+        """Wall-clock seconds of exactly `steps` calls after `warmup` untimed
+        ones, with a synchronisation on both sides, and the per-stage HIP-event
+        times (ms per call) of a pass of the same calls made before them.
+        That pass goes first so that the timed calls run at the clocks the
+        layer sustains: calls that start after the device has idled (input
+        generation, other workloads) run 10-20% slower for their first
+        milliseconds, which a short timed region would otherwise include."""
         torch, moe = self.torch, self.moe
+        moe.moe_stage_timing_enable(True)
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        ms, n = moe.moe_stage_timing_read()
+        moe.moe_stage_timing_enable(False)
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
@@ -229,13 +242,6 @@ class Workload:
             self.step()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        # per-stage HIP-event times over a second pass of the same steps
-        moe.moe_stage_timing_enable(True)
-        for _ in range(steps):
-            self.step()
-        torch.cuda.synchronize()
-        ms, n = moe.moe_stage_timing_read()
-        moe.moe_stage_timing_enable(False)
         return wall, {k: v / max(n, 1) for k, v in ms.items()}
 
     def per_call(self, steps):
@@ -363,8 +369,13 @@ def ceilings():
     """Measured ceilings of this device, beside the published peaks (context
     only: the roofline fractions are taken against the published peaks): the
     HBM read rate (moe_probe_read over a 2 GiB buffer, eight times the
-    infinity cache) and the sustained bf16 MFMA rate (moe_probe_mfma, 2 waves
-    per SIMD of 8 independent 16x16x32 chains); best of 5 timed runs each."""
+    infinity cache), the read rate of scattered expert blocks (moe_probe_gather:
+    200 of the 227 bf16 expert blocks of the 256-expert layer, 9.4 MB each,
+    that fit in 2 GiB, in a seeded order) and how it grows with the number of
+    workgroups reading (one per CU up to 256), the MXFP4 dequantisation stream
+    (moe_probe_mxfp4 over 1 GiB of codes and their scales) and the sustained
+    bf16 MFMA rate (moe_probe_mfma, 2 waves per SIMD of 8 independent
+    16x16x32 chains); best of 5 timed runs each."""
     import torch
 
     import routed_expert_ffn_moe_amd as moe
@@ -387,13 +398,37 @@ def ceilings():
     nbytes = 2 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     t_read = best_ms(lambda: moe.moe_probe_read(buf))
+    # scattered expert blocks: one bf16 expert (gate, up, down) of the
+    # 256-expert layer per chunk
+    chunk = 3 * 2048 * 768 * 2
+    pool_chunks = nbytes // chunk
+    import numpy as np
+    order = torch.from_numpy(np.random.default_rng(107).permutation(pool_chunks)[:200]
+                             .astype(np.int32)).cuda()
+    t_gather = best_ms(lambda: moe.moe_probe_gather(buf, chunk, order, 1024))
+    per_wg = {}
+    few = order[:24].contiguous()
+    for wgs in (8, 32, 64, 128, 256, 1024):
+        t = best_ms(lambda: moe.moe_probe_gather(buf, chunk, few, wgs))
+        per_wg[wgs] = round(few.numel() * chunk / (t * 1e-3) / 1e9, 1)
     del buf
+    nblk = (1 << 30) // 16
+    codes = torch.full((1 << 30,), 0x3B, dtype=torch.uint8, device="cuda")
+    scales = torch.full((nblk,), 120, dtype=torch.uint8, device="cuda")
+    sums = torch.empty(1024, dtype=torch.float32, device="cuda")
+    t_mx = best_ms(lambda: moe.moe_probe_mxfp4(codes, scales, sums))
+    del codes, scales
     waves = 8 * torch.cuda.get_device_properties(0).multi_processor_count
     iters = 20000
     t_mma = best_ms(lambda: moe.moe_probe_mfma(waves, iters))
     return {"hbm_read_GBps": round(nbytes / (t_read * 1e-3) / 1e9, 1),
+            "scattered_expert_read_GBps": round(order.numel() * chunk / (t_gather * 1e-3) / 1e9, 1),
+            "scattered_read_GBps_by_workgroups": per_wg,
+            "mxfp4_dequant_stream_GBps": round((1 << 30) * 17 / 16 / (t_mx * 1e-3) / 1e9, 1),
             "bf16_mfma_TFLOPs": round(waves * iters * 8 * 16384 / (t_mma * 1e-3) / 1e12, 1),
-            "probes": "moe_probe_read over 2 GiB; moe_probe_mfma, %d waves x %d rounds" % (waves, iters)}
+            "probes": "moe_probe_read over 2 GiB; moe_probe_gather, 200 expert blocks of %d B "
+                      "(24 for the workgroup counts); moe_probe_mxfp4 over 1 GiB of codes; "
+                      "moe_probe_mfma, %d waves x %d rounds" % (chunk, waves, iters)}
 
 
 def cpu_model():

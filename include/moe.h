@@ -219,6 +219,30 @@ int moe_stage_timing_read(float *ms, int n_stages, int *n_calls);
 int moe_probe_read(const void *buf, size_t bytes, void *stream);
 int moe_probe_mfma(int waves, int iters, int *sink, void *stream);
 
+/* Scattered expert-block reads ("MoE prefill quantum", the section ruling
+ * out the hardware, which times a random read of 300 blocks of 13.3 MB
+ * beside a sequential read).  pool: a device buffer of pool_bytes holding
+ * pool_bytes / chunk_bytes chunks of chunk_bytes (a positive multiple of 16;
+ * one expert's weight block); order: a device int32 array of nchunks chunk
+ * numbers (entries outside the pool read the nearest chunk); the chunks are
+ * read whole in that order by `wgs` workgroups of 256 threads (1..65536;
+ * fewer workgroups than CUs gives the read rate of that many CUs), 16-byte
+ * non-temporal loads, data discarded: nchunks * chunk_bytes bytes.
+ * moe_probe_mxfp4 streams nblocks MXFP4 blocks in the OCP row-major form
+ * (codes: 16 bytes per block, 32 E2M1 codes, the even element in the low
+ * nibble, 16-byte aligned; scales: one E8M0 byte per block), decodes every
+ * value as code x 2^(scale - 127) with the scaled fp4 conversion and adds
+ * them up: out[w] (a device float array of wgs entries) receives workgroup
+ * w's fp32 sum, so the stream is checkable; 17/32 byte per value ("MoE
+ * prefill quantum", the same section: unpacking and scaling MXFP4 streams
+ * at the raw read rate).  Both asynchronous on `stream`; MOE_EINVAL for bad
+ * sizes or NULL / misaligned pointers (checked before any launch), MOE_EHIP
+ * if the launch fails. */
+int moe_probe_gather(const void *pool, size_t pool_bytes, size_t chunk_bytes,
+                     const int32_t *order, int nchunks, int wgs, void *stream);
+int moe_probe_mxfp4(const void *codes, const uint8_t *scales, size_t nblocks, int wgs,
+                    float *out, void *stream);
+
 /* Static text for a return code. */
 const char *moe_strerror(int code);
 

@@ -21,6 +21,7 @@ __all__ = [
     "MOE_NOALLOC_SCRATCH_BYTES", "moe_route", "moe_strerror",
     "moe_last_error", "moe_stage_timing_enable", "moe_stage_timing_read", "moe_pack_bf16",
     "pack_bf16", "moe_pack_mxfp4", "pack_mxfp4", "STAGES", "moe_probe_read", "moe_probe_mfma",
+    "moe_probe_gather", "moe_probe_mxfp4",
     "lib_path", "load",
 ]
 
@@ -97,6 +98,11 @@ def load() -> ctypes.CDLL:
         lib.moe_probe_read.argtypes = [P, ctypes.c_size_t, P]
         lib.moe_probe_mfma.restype = ctypes.c_int
         lib.moe_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, P, P]
+        lib.moe_probe_gather.restype = ctypes.c_int
+        lib.moe_probe_gather.argtypes = [P, ctypes.c_size_t, ctypes.c_size_t, P, ctypes.c_int,
+                                         ctypes.c_int, P]
+        lib.moe_probe_mxfp4.restype = ctypes.c_int
+        lib.moe_probe_mxfp4.argtypes = [P, P, ctypes.c_size_t, ctypes.c_int, P, P]
         _lib = lib
     return _lib
 
@@ -243,6 +249,24 @@ def moe_probe_read(buf, stream=None) -> None:
 def moe_probe_mfma(waves: int, iters: int, stream=None) -> None:
     """bf16 MFMA chains on every wave (measurement aid, see moe.h)."""
     _check(load().moe_probe_mfma(waves, iters, None, _stream(stream)))
+
+
+def moe_probe_gather(pool, chunk_bytes: int, order, wgs: int, stream=None) -> None:
+    """Read the chunks of `pool` listed in the int32 device tensor `order`
+    (measurement aid, see moe.h)."""
+    n = pool.numel() * pool.element_size()
+    _check(load().moe_probe_gather(_ptr(pool), n, chunk_bytes, _ptr(order), order.numel(), wgs,
+                                   _stream(stream)))
+
+
+def moe_probe_mxfp4(codes, scales, out, stream=None) -> None:
+    """Decode and sum the MXFP4 blocks of `codes` / `scales` (row-major OCP
+    form); out (float32 device tensor) receives one sum per workgroup
+    (measurement aid, see moe.h)."""
+    nblk = scales.numel()
+    assert codes.numel() * codes.element_size() >= 16 * nblk
+    _check(load().moe_probe_mxfp4(_ptr(codes), _ptr(scales), nblk, out.numel(), _ptr(out),
+                                  _stream(stream)))
 
 
 def moe_strerror(code: int) -> str:

@@ -163,8 +163,13 @@ void launch_pack_bf16(int E, int N, int K, const uint16_t *w, uint16_t *out, hip
 // returns `code`: for entry points outside moe_api.cpp.
 int api_fail(int code, const char *what);
 
-// Measurement aids (probe.hip): the device's HBM read and bf16 MFMA ceilings.
+// Measurement aids (probe.hip): the device's HBM read (sequential and
+// scattered), MXFP4 dequantisation stream and bf16 MFMA ceilings.
 void launch_probe_read(const void *buf, size_t bytes, int *sink, hipStream_t st);
 void launch_probe_mfma(int waves, int iters, int *sink, hipStream_t st);
+void launch_probe_gather(const void *pool, int pool_chunks, const int32_t *order, int nchunks,
+                         size_t chunk_bytes, int wgs, int *sink, hipStream_t st);
+void launch_probe_mxfp4(const void *codes, const uint8_t *scales, size_t nblocks, int wgs,
+                        float *out, hipStream_t st);
 
 }  // namespace moe

@@ -706,6 +706,30 @@ int moe_probe_read(const void *buf, size_t bytes, void *stream)
     return launched("probe_read");
 }
 
+int moe_probe_gather(const void *pool, size_t pool_bytes, size_t chunk_bytes,
+                     const int32_t *order, int nchunks, int wgs, void *stream)
+{
+    if (!pool || !order || chunk_bytes == 0 || chunk_bytes % 16 != 0 || nchunks <= 0 ||
+        pool_bytes < chunk_bytes || pool_bytes / chunk_bytes > (size_t)INT32_MAX ||
+        (uintptr_t)pool % 16 != 0 || wgs <= 0 || wgs > 65536)
+        return fail(MOE_EINVAL, "moe_probe_gather: pool, order, chunk_bytes a positive multiple "
+                                "of 16 within pool_bytes, nchunks > 0, 1 <= wgs <= 65536");
+    moe::launch_probe_gather(pool, (int)(pool_bytes / chunk_bytes), order, nchunks, chunk_bytes,
+                             wgs, nullptr, (hipStream_t)stream);
+    return launched("probe_gather");
+}
+
+int moe_probe_mxfp4(const void *codes, const uint8_t *scales, size_t nblocks, int wgs, float *out,
+                    void *stream)
+{
+    if (!codes || !scales || !out || nblocks == 0 || (uintptr_t)codes % 16 != 0 || wgs <= 0 ||
+        wgs > 65536)
+        return fail(MOE_EINVAL, "moe_probe_mxfp4: codes (16-byte aligned), scales, out, "
+                                "nblocks > 0, 1 <= wgs <= 65536");
+    moe::launch_probe_mxfp4(codes, scales, nblocks, wgs, out, (hipStream_t)stream);
+    return launched("probe_mxfp4");
+}
+
 int moe_probe_mfma(int waves, int iters, int *sink, void *stream)
 {
     if (waves <= 0 || waves % 4 != 0 || iters <= 0)

@@ -226,3 +226,41 @@ def test_probe_argument_checks():
     assert lib.moe_probe_mfma(6, 10, None, None) == moe.MOE_EINVAL
     assert lib.moe_probe_mfma(8, 0, None, None) == moe.MOE_EINVAL
     assert "probe" in moe.moe_last_error()
+
+
+def test_scattered_and_mxfp4_probe_argument_checks():
+    """The scattered-read and MXFP4-stream probes check sizes, NULL and
+    misaligned pointers and workgroup counts before launching anything."""
+    lib = moe.load()
+    P = ctypes.c_void_p
+    pool, order, out = P(0x7F1000000000), P(0x7F2000000000), P(0x7F3000000000)
+    mb = 1 << 20
+    ok = (pool, 64 * mb, mb, order, 8, 256, None)
+    bad = [
+        (None,) + ok[1:],                       # no pool
+        ok[:3] + (None,) + ok[4:],              # no order
+        ok[:2] + (0,) + ok[3:],                 # empty chunk
+        ok[:2] + (mb + 8,) + ok[3:],            # chunk not a multiple of 16
+        (pool, mb // 2, mb) + ok[3:],           # chunk larger than the pool
+        ok[:4] + (0,) + ok[5:],                 # no chunks
+        ok[:5] + (0, None),                     # no workgroups
+        ok[:5] + (65537, None),                 # too many workgroups
+        (P(0x7F1000000008),) + ok[1:],          # misaligned pool
+    ]
+    for args in bad:
+        assert lib.moe_probe_gather(*args) == moe.MOE_EINVAL, args
+        assert "moe_probe_gather" in moe.moe_last_error()
+    codes, scales = P(0x7F4000000000), P(0x7F5000000000)
+    okm = (codes, scales, 1 << 16, 256, out, None)
+    badm = [
+        (None,) + okm[1:],
+        (codes, None) + okm[2:],
+        okm[:4] + (None, None),
+        okm[:2] + (0,) + okm[3:],
+        okm[:3] + (0,) + okm[4:],
+        okm[:3] + (70000,) + okm[4:],
+        (P(0x7F4000000004),) + okm[1:],
+    ]
+    for args in badm:
+        assert lib.moe_probe_mxfp4(*args) == moe.MOE_EINVAL, args
+        assert "moe_probe_mxfp4" in moe.moe_last_error()

@@ -696,3 +696,36 @@ def test_measurement_probes_run():
     moe.moe_probe_read(buf)
     moe.moe_probe_mfma(8, 16)
     torch.cuda.synchronize()
+
+
+def test_scattered_read_probe_runs():
+    """The scattered expert-block read probe reads the chunks a seeded order
+    lists, with many workgroups and with a few."""
+    chunk = 1 << 16
+    pool = torch.ones((64 * chunk) // 4, dtype=torch.int32, device="cuda")
+    order = torch.from_numpy(np.random.default_rng(5).permutation(64)[:40].astype(np.int32)).cuda()
+    for wgs in (1, 8, 1024):
+        moe.moe_probe_gather(pool, chunk, order, wgs)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("wgs", [1, 8, 300])
+def test_mxfp4_stream_probe_sums_the_decoded_values(wgs):
+    """The MXFP4 dequantisation stream decodes what the oracle decodes: the
+    workgroups' sums add up to the sum of the oracle's decoded values (the
+    sum is independent of the order of values within a block, so this pins
+    the code table and the scale of every block; the element order is pinned
+    by the MXFP4 layer's parity)."""
+    N, K = 96, 1024                      # 3072 blocks of 32
+    codes, scales = mi.mxfp4_quantize(
+        torch.from_numpy(np.random.default_rng(11).standard_normal((N, K)).astype(np.float32) * 0.02))
+    codes_h, scales_h = mi.to_host(codes), mi.to_host(scales)
+    want = oracle.decode(codes_h, "mxfp4", N, K, scales_h)
+    out = torch.zeros(wgs, dtype=torch.float32, device="cuda")
+    moe.moe_probe_mxfp4(torch.from_numpy(codes_h).cuda(), torch.from_numpy(scales_h).cuda(), out)
+    torch.cuda.synchronize()
+    got = float(out.double().sum())
+    ref = float(want.astype(np.float64).sum())
+    scale = float(np.abs(want).astype(np.float64).sum())
+    say("[probe] mxfp4 stream sum", got, "oracle", ref, "sum|v|", scale)
+    assert abs(got - ref) <= 1e-5 * scale, (got, ref)
