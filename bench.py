@@ -219,15 +219,28 @@ class Workload:
         self.i += 1
         self.moe.moe_forward(self.shape, wt, self.x, self.y, self.idx, self.w, self.ws)
 
+    def warm(self, seconds=0.05):
+        """Untimed bursts of 10 calls until `seconds` have passed: calls that
+        start after the device has idled (input generation, another
+        workload) run 10-20% slower for their first milliseconds."""
+        t0 = time.perf_counter()
+        while True:
+            for _ in range(10):
+                self.step()
+            self.torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                return
+
     def time(self, steps, warmup):
         """Wall-clock seconds of exactly `steps` calls after `warmup` untimed
         ones, with a synchronisation on both sides, and the per-stage HIP-event
         times (ms per call) of a pass of the same calls made before them.
-        That pass goes first so that the timed calls run at the clocks the
-        layer sustains: calls that start after the device has idled (input
-        generation, other workloads) run 10-20% slower for their first
-        milliseconds, which a short timed region would otherwise include."""
+        Untimed warm-up bursts precede the stage pass, and the stage pass
+        precedes the timed calls, so that both run at the clocks the layer
+        sustains rather than in the slower first milliseconds after the
+        device has idled."""
         torch, moe = self.torch, self.moe
+        self.warm()
         moe.moe_stage_timing_enable(True)
         for _ in range(steps):
             self.step()
