@@ -59,10 +59,13 @@ __global__ __launch_bounds__(256) void permute_hist(const int32_t *__restrict__ 
         blk[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// One workgroup: counts, offsets (exclusive prefix in LDS), per-block start
-// positions (written over blk), the shared-expert group and both tile lists.
-// With idx given (nblk * E <= FUSED_HIST) it counts the blocks' pairs itself.
-__global__ __launch_bounds__(1024) void permute_scan(
+// One workgroup of 1024 threads: counts, offsets (exclusive prefix in LDS),
+// the shared-expert group and both tile lists; with POS also the per-block
+// start positions (written over blk), and with idx given (nblk * E <=
+// FUSED_HIST) it counts the blocks' pairs itself.  Without POS blk is only
+// read (the scatter workgroups of permute_place read it at the same time).
+template <bool POS>
+__device__ __forceinline__ void scan_groups(
     const int32_t *__restrict__ idx,
     int32_t *__restrict__ blk, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     Tile *__restrict__ tiles_a, int32_t *__restrict__ ntiles_a, Tile *__restrict__ tiles_b,
@@ -76,11 +79,26 @@ __global__ __launch_bounds__(1024) void permute_scan(
     __shared__ int32_t s_off[1025];
     __shared__ int32_t s_warp[3][16];
     __shared__ int32_t s_nt[2];
-    __shared__ int32_t s_blk[FUSED_HIST];
+    __shared__ int32_t s_blk[POS ? FUSED_HIST : 1];
     const int tid = threadIdx.x;
     const int G = E + (shared ? 1 : 0);  // groups
     constexpr int SCH = 16;
-    if (idx) {
+    if constexpr (!POS) {
+        // column sums over blocks only
+        for (int e = tid; e < E; e += 1024) {
+            int run = 0;
+            for (int b0 = 0; b0 < nblk; b0 += SCH) {
+                int c[SCH];
+#pragma unroll
+                for (int i = 0; i < SCH; ++i)
+                    c[i] = b0 + i < nblk ? blk[(int64_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+                for (int i = 0; i < SCH; ++i)
+                    run += c[i];
+            }
+            s_cnt[e] = run;
+        }
+    } else if (idx) {
         // Per-block histograms in LDS, then their running prefixes in place.
         for (int i = tid; i < nblk * E; i += 1024)
             s_blk[i] = 0;
@@ -187,6 +205,7 @@ __global__ __launch_bounds__(1024) void permute_scan(
     }
     __syncthreads();
     // Per-block start positions inside each expert's range.
+    if constexpr (POS)
     for (int e = tid; e < E; e += 1024) {
         const int o = s_off[e];
         if (idx) {
@@ -236,6 +255,130 @@ __global__ __launch_bounds__(1024) void permute_scan(
                 items[ntn * st[g] + nt * nt_g + m] = int4{g, r0, nr, nt * wrows};
         }
     }
+}
+
+__global__ __launch_bounds__(1024) void permute_scan(
+    const int32_t *__restrict__ idx,
+    int32_t *__restrict__ blk, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    Tile *__restrict__ tiles_a, int32_t *__restrict__ ntiles_a, Tile *__restrict__ tiles_b,
+    int32_t *__restrict__ ntiles_b, int bm_a, int bm_b, int nblk, int E, int n_pairs, int T,
+    int shared, int4 *__restrict__ items_a, int ntn_a, int wrows_a, int4 *__restrict__ items_b,
+    int ntn_b, int wrows_b)
+{
+    scan_groups<true>(idx, blk, counts, offsets, tiles_a, ntiles_a, tiles_b, ntiles_b, bm_a, bm_b,
+                      nblk, E, n_pairs, T, shared, items_a, ntn_a, wrows_a, items_b, ntn_b, wrows_b);
+}
+
+// One block of PAIRS_PER_BLOCK pairs placed by 1024 threads, one pair each,
+// without a separate scan pass: the block's first position in each expert's
+// range is the expert's offset (exclusive prefix over the experts of the
+// column sums of the block histograms) plus that expert's pairs in the
+// earlier blocks, both formed here from the histograms; inside the block the
+// waves follow in order and a wave's lanes with equal experts are ranked by
+// a ballot-built match mask.  The same grouped order as permute_scatter (t,
+// then j, within every expert).
+__device__ __forceinline__ void place_block(const int32_t *__restrict__ idx,
+                                            const int32_t *__restrict__ blk, int nblk, int b,
+                                            int32_t *__restrict__ row_src,
+                                            int32_t *__restrict__ row_tok,
+                                            int32_t *__restrict__ row_of, int n_pairs, int E,
+                                            int T, int k, int shared)
+{
+    static_assert(PAIRS_PER_BLOCK == 1024, "one pair per thread");
+    __shared__ int32_t s_start[1024];
+    __shared__ uint16_t s_wc[16][1024];  // per wave and expert: pairs, then pairs in earlier waves
+    __shared__ int32_t s_wsum[16];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int p = b * PAIRS_PER_BLOCK + tid;
+    const int e = p < n_pairs ? idx[p] : -1;
+    constexpr int SCH = 16;
+    // column sums over all blocks (the expert's rows) and over those before b
+    int tot = 0, pre = 0;
+    if (tid < E) {
+        for (int b0 = 0; b0 < nblk; b0 += SCH) {
+            int c[SCH];
+#pragma unroll
+            for (int i = 0; i < SCH; ++i)  // all reads in flight together
+                c[i] = b0 + i < nblk ? blk[(int64_t)(b0 + i) * E + tid] : 0;
+#pragma unroll
+            for (int i = 0; i < SCH; ++i) {
+                tot += c[i];
+                pre += b0 + i < b ? c[i] : 0;
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+        s_wc[q][tid] = 0;
+    // exclusive prefix of the experts' rows
+    const int inc = wave_scan_add(tot);
+    if (lane == 63)
+        s_wsum[wv] = inc;
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w)
+        before += w < wv ? s_wsum[w] : 0;
+    if (tid < E)
+        s_start[tid] = before + inc - tot + pre;
+    // rank among this wave's earlier pairs of the same expert
+    const bool valid = e >= 0;
+    uint64_t same = __ballot(valid);
+    for (int bit = 0; bit < 10; ++bit) {
+        const bool on = (e >> bit) & 1;
+        const uint64_t ones = __ballot(valid && on);
+        same &= on ? ones : ~ones;
+    }
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(same & below);
+    if (valid && rank == 0)  // one writer per wave and expert
+        s_wc[wv][e] = (uint16_t)__popcll(same);
+    __syncthreads();
+    if (tid < E) {
+        int run = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+            const int c = s_wc[w][tid];
+            s_wc[w][tid] = (uint16_t)run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    if (valid) {
+        const int pos = s_start[e] + s_wc[wv][e] + rank;
+        row_src[pos] = p;
+        row_tok[pos] = p / k;
+        row_of[p] = pos;
+    }
+    // shared-expert rows follow the routed ones, in token order
+    if (shared && b == 0) {
+        for (int t = tid; t < T; t += 1024) {
+            row_src[n_pairs + t] = n_pairs + t;
+            row_tok[n_pairs + t] = t;
+        }
+    }
+}
+
+// The permutation of a pass whose block histograms are counted already (by
+// the segmented router's top-k kernel), in one launch: workgroups 0 ..
+// nblk-1 place their blocks' pairs (place_block) while workgroup nblk forms
+// the counts, offsets, tile lists and work items (scan_groups without the
+// per-block positions, reading the histograms the others read too).
+__global__ __launch_bounds__(1024) void permute_place(
+    const int32_t *__restrict__ idx, int32_t *__restrict__ blk, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, Tile *__restrict__ tiles_a, int32_t *__restrict__ ntiles_a,
+    Tile *__restrict__ tiles_b, int32_t *__restrict__ ntiles_b, int bm_a, int bm_b, int nblk,
+    int E, int n_pairs, int T, int shared, int4 *__restrict__ items_a, int ntn_a, int wrows_a,
+    int4 *__restrict__ items_b, int ntn_b, int wrows_b, int32_t *__restrict__ row_src,
+    int32_t *__restrict__ row_tok, int32_t *__restrict__ row_of, int k)
+{
+    if ((int)blockIdx.x == nblk) {  // uniform
+        scan_groups<false>(nullptr, blk, counts, offsets, tiles_a, ntiles_a, tiles_b, ntiles_b,
+                           bm_a, bm_b, nblk, E, n_pairs, T, shared, items_a, ntn_a, wrows_a,
+                           items_b, ntn_b, wrows_b);
+        return;
+    }
+    place_block(idx, blk, nblk, blockIdx.x, row_src, row_tok, row_of, n_pairs, E, T, k, shared);
 }
 
 // Stable scatter.  Each of a block's 4 waves walks a quarter of its pairs 64
@@ -320,6 +463,13 @@ void launch_permute(const PermuteArgs &a, hipStream_t st)
 {
     const int n_pairs = a.T * a.k;
     const int nblk = permute_blocks(n_pairs);
+    if (a.hist_done && nblk > 0 && a.E <= 1024) {
+        permute_place<<<nblk + 1, 1024, 0, st>>>(
+            a.idx, a.blk, a.counts, a.offsets, a.tiles_a, a.ntiles_a, a.tiles_b, a.ntiles_b,
+            a.bm_a, a.bm_b, nblk, a.E, n_pairs, a.T, a.shared, a.items_a, a.ntn_a, a.wrows_a,
+            a.items_b, a.ntn_b, a.wrows_b, a.row_src, a.row_tok, a.row_of, a.k);
+        return;
+    }
     const bool fused = !a.hist_done && nblk * a.E <= FUSED_HIST;
     if (nblk > 0 && !fused && !a.hist_done)
         permute_hist<<<nblk, 256, a.E * sizeof(int32_t), st>>>(a.idx, a.blk, n_pairs, a.E);
