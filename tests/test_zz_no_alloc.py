@@ -35,8 +35,11 @@ def test_noalloc_refuses_passes_beyond_its_scratch():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("name,T1,T2", [("c1", 128, 40), ("c4_t6", 6, 1)])
+@pytest.mark.parametrize("name,T1,T2", [("c1", 128, 40), ("c1", 600, 300), ("c4_t6", 6, 1)])
 def test_noalloc_matches_forward_on_two_calls(name, T1, T2):
+    """Short passes (T <= 128: the one-launch routing), long passes (T = 600
+    and 300: the segmented router and the one-launch permutation over 5 and
+    3 blocks) and the MXFP4 decode rows."""
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         pytest.skip("no GPU visible")
