@@ -125,6 +125,33 @@ def test_forward_parity(name):
     assert err <= hx.TIGHT[c["w"]], err
 
 
+@pytest.mark.parametrize("name,T,k", [("c1", 128, 1), ("c1", 128, 6), ("c1", 600, 4),
+                                      ("c1", 600, 1), ("c4_t6", 6, 4), ("c4_t1", 1, 2)])
+def test_run_time_top_k_on_the_same_layer(name, T, k):
+    """The experts-per-token count overridden at run time on the same packed
+    weights (the pages' decode experiments run one model with fewer experts
+    per token): the short-pass routing (T=128), the segmented router and the
+    one-launch permutation (T=600) and the MXFP4 decode-row kernels (T=6, 1)
+    with k other than the layer's 8 - routing bit-exact, weights within
+    1e-5 (exactly 1 for k=1), y against the oracle run with that k."""
+    import copy
+    c0, g = layer(name)
+    c = dict(c0, top_k=k, T=T, seed=4100 + 10 * T + k)
+    gk = copy.copy(g)
+    gk.c = c
+    x = hx.margin_x(c, g.lay)
+    y, idx, w = gk.forward(hx.act_torch(x, c["act"], "cuda"))
+    idx_r, w_r, _ = oracle.route(hx.router_only_layer(c, g.lay), x)
+    assert np.array_equal(idx.cpu().numpy(), idx_r)
+    assert np.abs(w.cpu().numpy() - w_r).max() <= hx.W_TOL
+    if k == 1:
+        assert bool((w == 1.0).all())
+    experts = sorted(set(idx_r.reshape(-1).tolist()))
+    y_ref, _, _ = oracle.forward(hx.oracle_layer(c, g.lay, experts), x)
+    check_err("top_k=%d on %s, T=%d" % (k, name, T), hx.rel_err(hx.y_host(y, c["act"]), y_ref),
+              c["w"])
+
+
 @pytest.mark.parametrize("name,T", [("c1", None), ("c1", 16), ("c1", 129), ("c2", None),
                                     ("c1", 9000), ("c1", 20000)])
 def test_route_and_permutation_bit_exact(name, T):
