@@ -23,6 +23,8 @@ constexpr int PAIRS_PER_BLOCK = PERMUTE_PAIRS_PER_BLOCK;
 // Passes whose per-block histograms fit in this many LDS counters build them
 // inside the scan kernel (one launch less).
 constexpr int FUSED_HIST = 8192;
+// Most permutation blocks placed by permute_place (see launch_permute).
+constexpr int PLACE_MAX_BLOCKS = 256;
 
 // Orders one wave's LDS accesses across its lanes (no other wave shares
 // the data).
@@ -463,7 +465,11 @@ void launch_permute(const PermuteArgs &a, hipStream_t st)
 {
     const int n_pairs = a.T * a.k;
     const int nblk = permute_blocks(n_pairs);
-    if (a.hist_done && nblk > 0 && a.E <= 1024) {
+    // Each placing workgroup sums the histograms of all blocks, so the work
+    // and L2 reads of the one-launch form grow as nblk^2: beyond 256 blocks
+    // (T*k > 262,144 pairs; the sweep's T=65,536 was 3% slower with it) the
+    // separate scan, whose one workgroup forms the prefixes once, is used.
+    if (a.hist_done && nblk > 0 && nblk <= PLACE_MAX_BLOCKS && a.E <= 1024) {
         permute_place<<<nblk + 1, 1024, 0, st>>>(
             a.idx, a.blk, a.counts, a.offsets, a.tiles_a, a.ntiles_a, a.tiles_b, a.ntiles_b,
             a.bm_a, a.bm_b, nblk, a.E, n_pairs, a.T, a.shared, a.items_a, a.ntn_a, a.wrows_a,

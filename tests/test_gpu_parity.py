@@ -153,14 +153,15 @@ def test_run_time_top_k_on_the_same_layer(name, T, k):
 
 
 @pytest.mark.parametrize("name,T", [("c1", None), ("c1", 16), ("c1", 129), ("c2", None),
-                                    ("c1", 9000), ("c1", 20000)])
+                                    ("c1", 9000), ("c1", 20000), ("c1", 33000)])
 def test_route_and_permutation_bit_exact(name, T):
     """T=128 and 16: the short-pass kernels with eight and one route
     workgroups; T=129: the long-pass kernels, two permutation blocks (the
     second holding 8 pairs); T=2048 (Zipf), 9000 and 20,000 at top-8: 16, 71
     (the last one partial) and 157 blocks of 1,024 pairs placed by
     permute_place, each block forming its own start positions from the
-    histograms of all the blocks before it."""
+    histograms of all the blocks before it; T=33,000: 258 blocks, past
+    permute_place's limit, so the separate scan and scatter place them."""
     say("[route]", name, T)
     c, g = layer(name)
     if T is not None:
