@@ -132,12 +132,12 @@ __device__ __forceinline__ Item item_at(const int4 *__restrict__ items, int wi)
 }
 
 // Element offsets (into x or h) of the token rows this thread stages.
-template <int ACH, bool GU, int SKC>
+template <int ACH, bool GU, int SKC, int NT>
 __device__ __forceinline__ void item_rows(const StreamP &p, const Item &it, int tid, int (&aro)[ACH])
 {
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
-        const int pos = it.row0 + min((tid + 256 * i) / (SKC / 8), it.nrows - 1);
+        const int pos = it.row0 + min((tid + NT * i) / (SKC / 8), it.nrows - 1);
         aro[i] = GU ? p.row_tok[pos] * p.H : pos * p.ldh;
     }
 }
@@ -402,21 +402,29 @@ __device__ __forceinline__ void kchunk_w4(bool full, const uint16_t *As, int slo
 // the LDS and L2 latency that one wave's own schedule cannot.
 constexpr int wg_per_cu(int bm) { return bm <= 16 ? 3 : bm <= 64 ? 2 : 1; }
 
-template <int BM, bool GU, int SD, int SKC, bool W4, int TL, bool WIDE>
-__global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
-                                                                    const int4 *__restrict__ items)
+// NWV waves per workgroup: 4 (one per SIMD), or 8 for the 128-row bf16
+// tiles - two per SIMD, each with half the weight rows of the tile, so that
+// one wave's matrix instructions issue beside the other's memory
+// instructions; the tile, and every output's sum over K, stay the same.
+template <int BM, bool GU, int SD, int SKC, bool W4, int TL, bool WIDE, int NWV>
+__global__ __launch_bounds__(64 * NWV, NWV == 8 ? 1 : wg_per_cu(BM)) void expert_stream(
+    StreamP p, const int4 *__restrict__ items)
 {
+    constexpr int NT = 64 * NWV;               // threads
     constexpr int SLD = sld_of(SKC), SPC = SKC / 32, RW = SKC / 8;  // 16-byte pieces per row
     constexpr int NB = GU ? 2 : 1;             // weight matrices
-    constexpr int CB = (GU ? 2 : 4) * (WIDE ? 2 : 1);  // 16-row weight blocks per wave and matrix
+    // 16-row weight blocks per wave and matrix
+    constexpr int CB = (GU ? 2 : 4) * (WIDE ? 2 : 1) * 4 / NWV;
     constexpr int MB = BM / 16;                // 16-row token blocks
-    constexpr int ACH = BM * (SKC / 8) / 256;  // 16-byte token chunks per thread
+    constexpr int ACH = BM * (SKC / 8) / NT;   // 16-byte token chunks per thread
     static_assert(W4 || SD == 4 || SD == 8 || (WIDE && SD == 2), "prefetch ring depth in K steps");
     static_assert(!WIDE || (BM == 128 && !W4), "wide tiles: 128 bf16 rows");
     static_assert(W4 || (2 * SPC) % SD == 0, "ring slots line up with chunk pairs");
     static_assert(!W4 || (SD == 2 && SKC == 128), "MXFP4: a ring of two 128-K chunks");
-    static_assert(ACH >= 1 && ACH * 256 == BM * SKC / 8, "token staging");
-    static_assert(CB % 2 == 0 && 4 * CB * 16 == wrows_of(GU, WIDE), "column blocks go in pairs");
+    static_assert(ACH >= 1 && ACH * NT == BM * SKC / 8, "token staging");
+    static_assert(NWV == 4 || (NWV == 8 && BM == 128 && !W4 && !WIDE), "eight waves: 128-row bf16 tiles");
+    static_assert((CB % 2 == 0 || NWV == 8) && NWV * CB * 16 == wrows_of(GU, WIDE),
+                  "column blocks go in pairs (one block per wave with eight waves)");
     // the 128-row tiles' accumulators fill the accumulation registers
     constexpr bool AGPR = BM >= 128;
 
@@ -459,7 +467,8 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
             woff[cb] = (wave * CB + cb) * Q4 * 1024 + lane * 16;  // bytes
             soff[cb] = ((wave * CB + cb) * 64 + lane) * Q4;
         } else {
-            woff[cb] = ((wave * CB / 2 + cb / 2) * (K / 32) * 2 + (cb & 1)) * 512 + lane * 8;
+            const int gb = wave * CB + cb;  // 16-row block of the item's slice
+            woff[cb] = ((gb >> 1) * (K / 32) * 2 + (gb & 1)) * 512 + lane * 8;
             soff[cb] = 0;
         }
     }
@@ -478,7 +487,7 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
     int aoff[ACH];
 #pragma unroll
     for (int i = 0; i < ACH; ++i)
-        aoff[i] = ((tid + 256 * i) / RW) * SLD + (tid % RW) * 8;
+        aoff[i] = ((tid + NT * i) / RW) * SLD + (tid % RW) * 8;
 
     // Prologue: first item's weights for chunk 0, its token rows, chunk 0 in LDS.
     Item cur = item_at(items, base + slot);
@@ -509,8 +518,8 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
                 }
             }
     int aro[ACH], aro_n[ACH];
-    item_rows<ACH, GU, SKC>(p, cur, tid, aro);
-    item_rows<ACH, GU, SKC>(p, nxt, tid, aro_n);
+    item_rows<ACH, GU, SKC, NT>(p, cur, tid, aro);
+    item_rows<ACH, GU, SKC, NT>(p, nxt, tid, aro_n);
     // Token chunks in flight: TL (1 or 2) ahead of the one in LDS.
     static_assert(TL == 1 || TL == 2, "token chunks in flight");
     u32v<ACH> rt[TL];
@@ -637,6 +646,14 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
                     }
                     *(uint2 *)(p.out + (int64_t)pos * (GU ? p.ldh : p.H) + n4 + 16 * cb) = o;
                 }
+            } else if (GU && CB == 1) {
+                // block wave & 1 of 32-row group wave / 2: 4 adjacent columns
+                const int n1 = cur.n0 + 32 * (wave >> 1) + 8 * lg + 4 * (wave & 1);
+                const floatx4 g = acc[0][0][mb], u = acc[NB - 1][0][mb];
+                uint2 o;
+                o.x = pack_bf2(silu(g[0]) * u[0], silu(g[1]) * u[1]);
+                o.y = pack_bf2(silu(g[2]) * u[2], silu(g[3]) * u[3]);
+                *(uint2 *)(p.out + (int64_t)pos * p.ldh + n1) = o;
             } else if (GU) {
 #pragma unroll
                 for (int q = 0; q < CB / 2; ++q) {
@@ -672,7 +689,7 @@ __global__ __launch_bounds__(256, wg_per_cu(BM)) void expert_stream(StreamP p,
 #pragma unroll
         for (int i = 0; i < ACH; ++i)
             aro[i] = aro_n[i];
-        item_rows<ACH, GU, SKC>(p, nxt, tid, aro_n);
+        item_rows<ACH, GU, SKC, NT>(p, nxt, tid, aro_n);
     }
 }
 
@@ -688,7 +705,7 @@ int device_cus()
     return cus;
 }
 
-template <int BM, bool GU, int SD, int SKC, bool W4, int TL, bool WIDE = false>
+template <int BM, bool GU, int SD, int SKC, bool W4, int TL, bool WIDE = false, int NWV = 4>
 void run(const ExpertArgs &a, hipStream_t st)
 {
     StreamP p;
@@ -726,7 +743,7 @@ void run(const ExpertArgs &a, hipStream_t st)
     int &occ = per_cu[GU ? 1 : 0];
     if (!occ) {
         int b = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, expert_stream<BM, GU, SD, SKC, W4, TL, WIDE>, 256,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, expert_stream<BM, GU, SD, SKC, W4, TL, WIDE, NWV>, 64 * NWV,
                                                          0) != hipSuccess ||
             b < 1)
             b = 1;
@@ -734,7 +751,7 @@ void run(const ExpertArgs &a, hipStream_t st)
     }
     const int64_t per_xcd = (items + 7) / 8;
     const int64_t slots = std::min<int64_t>(per_xcd, (int64_t)(cus / 8) * occ);
-    expert_stream<BM, GU, SD, SKC, W4, TL, WIDE><<<(unsigned)(slots * 8), 256, 0, st>>>(p, p.items);
+    expert_stream<BM, GU, SD, SKC, W4, TL, WIDE, NWV><<<(unsigned)(slots * 8), 64 * NWV, 0, st>>>(p, p.items);
 }
 
 }  // namespace
@@ -869,9 +886,33 @@ static int stream_tl_w4()
     return forced ? forced : 2;
 }
 
+// Waves per workgroup of the 128-row bf16 tiles: eight for the down
+// projection (T=2048 layer: down 106.1 -> 103.5 us, the same results bit for
+// bit), four for gate+up (unchanged at eight: 170.0 vs 169.4 us); a ring of
+// eight K steps with eight waves spills.  MOE_STREAM_NWV (4 or 8) overrides
+// both for tuning runs (read once per process).
+static int stream_nwv(bool gu)
+{
+    static const int forced = [] {
+        const char *e = getenv("MOE_STREAM_NWV");
+        const int v = e ? atoi(e) : 0;
+        return (v == 4 || v == 8) ? v : 0;
+    }();
+    return forced ? forced : (gu ? 4 : 8);
+}
+
 template <int BM, bool GU, int SKC>
 static void run_skc(const ExpertArgs &a, hipStream_t st)
 {
+    if constexpr (BM == 128 && SKC == 128) {
+        if (stream_nwv(GU) == 8) {
+            if (stream_sd(BM) == 4)
+                run<BM, GU, 4, SKC, false, 1, false, 8>(a, st);
+            else
+                run<BM, GU, 8, SKC, false, 1, false, 8>(a, st);
+            return;
+        }
+    }
     if (stream_sd(BM) == 8)
         run<BM, GU, 8, SKC, false, 1>(a, st);
     else
