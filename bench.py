@@ -69,17 +69,44 @@ def stage_work(c, counts, fused_down_combine=False):
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 
 
+def source_code_text(src):
+    """C/C++/HIP source text with its comments removed and its whitespace
+    collapsed (string and character literals kept as they are)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+            out.append(" ")
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_sources_sha1():
-    """Digest of the HIP sources: counter readings taken from other sources
-    no longer describe the kernels that run."""
+    """Digest of the HIP sources' code (comments and whitespace left out):
+    counter readings taken from other code no longer describe the kernels
+    that run."""
     import hashlib
     d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "routed_expert_ffn_moe_amd", "csrc")
     h = hashlib.sha1()
     for f in sorted(os.listdir(d)):
         if f.endswith((".hip", ".h", ".cpp")):
             h.update(f.encode())
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(fh.read())
+            with open(os.path.join(d, f), encoding="utf-8", errors="surrogateescape") as fh:
+                h.update(source_code_text(fh.read()).encode("utf-8", "surrogateescape"))
     return h.hexdigest()
 
 

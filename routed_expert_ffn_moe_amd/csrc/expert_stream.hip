@@ -18,7 +18,10 @@
 //    contiguous kilobyte, so each load instruction of a wave fetches whole
 //    cache lines (row-major rows would give 64 bytes of each of 16 lines).
 //  * The tile's token rows (gathered through row_tok) are staged in LDS in
-//    double-buffered 128- or 256-wide K chunks shared by the 4 waves.
+//    double-buffered 128- or 256-wide K chunks shared by the 4 waves.  The
+//    128-row down tiles run 8 waves instead, two per SIMD, each with half
+//    the weight rows (16 of the 32 of a 4-wave wave's pair of blocks, or 32
+//    of 64): the same tile and the same MFMAs per output.
 //  * The MFMA takes the weights as its A operand and the tokens as B; with
 //    the weight rows of the two blocks of a 32-row group interleaved by fours,
 //    a lane ends up with 8 adjacent output columns of one token row and

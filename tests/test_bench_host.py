@@ -136,3 +136,15 @@ def test_per_call_quantiles():
     q = bench.quantiles([float(v) for v in range(100, 0, -1)])  # 1..100 in any order
     assert q == {"calls": 100, "median": 51.0, "p10": 11.0, "p90": 90.0}
     assert bench.quantiles([7.0]) == {"calls": 1, "median": 7.0, "p10": 7.0, "p90": 7.0}
+
+
+def test_source_digest_ignores_comments_and_layout():
+    """The digest that ties counter records to the kernels covers code only:
+    comments and whitespace leave it unchanged, string literals and code do
+    not."""
+    a = 'int f(int x) { return x + 1; } // one\n/* two\n */ const char *s = "// kept";'
+    b = 'int f(int x)\n{\n    return x + 1;  /* other words */\n}\nconst char *s = "// kept";'
+    assert bench.source_code_text(a) == bench.source_code_text(b)
+    assert bench.source_code_text(a) != bench.source_code_text(a.replace("x + 1", "x + 2"))
+    assert bench.source_code_text(a) != bench.source_code_text(a.replace('"// kept"', '"// gone"'))
+    assert '"// kept"' in bench.source_code_text(a)
