@@ -19,7 +19,8 @@
 //    cache lines (row-major rows would give 64 bytes of each of 16 lines).
 //  * The tile's token rows (gathered through row_tok) are staged in LDS in
 //    double-buffered 128- or 256-wide K chunks shared by the 4 waves.  The
-//    128-row down tiles run 8 waves instead, two per SIMD, each with half
+//    128-row bf16 down tiles and both 128-row MXFP4 tiles run 8 waves
+//    instead, two per SIMD, each with half
 //    the weight rows (16 of the 32 of a 4-wave wave's pair of blocks, or 32
 //    of 64): the same tile and the same MFMAs per output.
 //  * The MFMA takes the weights as its A operand and the tokens as B; with
@@ -405,10 +406,11 @@ __device__ __forceinline__ void kchunk_w4(bool full, const uint16_t *As, int slo
 // the LDS and L2 latency that one wave's own schedule cannot.
 constexpr int wg_per_cu(int bm) { return bm <= 16 ? 3 : bm <= 64 ? 2 : 1; }
 
-// NWV waves per workgroup: 4 (one per SIMD), or 8 for the 128-row bf16
-// tiles - two per SIMD, each with half the weight rows of the tile, so that
-// one wave's matrix instructions issue beside the other's memory
-// instructions; the tile, and every output's sum over K, stay the same.
+// NWV waves per workgroup: 4 (one per SIMD), or 8 for the 128-row narrow
+// tiles (bf16 or MXFP4 weights) - two per SIMD, each with half the weight
+// rows of the tile, so that one wave's matrix instructions issue beside the
+// other's memory instructions; the tile, and every output's sum over K,
+// stay the same.
 template <int BM, bool GU, int SD, int SKC, bool W4, int TL, bool WIDE, int NWV>
 __global__ __launch_bounds__(64 * NWV, NWV == 8 ? 1 : wg_per_cu(BM)) void expert_stream(
     StreamP p, const int4 *__restrict__ items)
@@ -425,7 +427,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 8 ? 1 : wg_per_cu(BM)) void expert
     static_assert(W4 || (2 * SPC) % SD == 0, "ring slots line up with chunk pairs");
     static_assert(!W4 || (SD == 2 && SKC == 128), "MXFP4: a ring of two 128-K chunks");
     static_assert(ACH >= 1 && ACH * NT == BM * SKC / 8, "token staging");
-    static_assert(NWV == 4 || (NWV == 8 && BM == 128 && !W4 && !WIDE), "eight waves: 128-row bf16 tiles");
+    static_assert(NWV == 4 || (NWV == 8 && BM == 128 && !WIDE), "eight waves: 128-row narrow tiles");
     static_assert((CB % 2 == 0 || NWV == 8) && NWV * CB * 16 == wrows_of(GU, WIDE),
                   "column blocks go in pairs (one block per wave with eight waves)");
     // the 128-row tiles' accumulators fill the accumulation registers
@@ -889,26 +891,29 @@ static int stream_tl_w4()
     return forced ? forced : 2;
 }
 
-// Waves per workgroup of the 128-row bf16 tiles: eight for the down
-// projection (T=2048 layer: down 106.1 -> 103.5 us, the same results bit for
-// bit), four for gate+up (unchanged at eight: 170.0 vs 169.4 us); a ring of
-// eight K steps with eight waves spills.  MOE_STREAM_NWV (4 or 8) overrides
-// both for tuning runs (read once per process).
-static int stream_nwv(bool gu)
+// Waves per workgroup of the 128-row narrow tiles.  bf16 weights: eight for
+// the down projection (T=2048 layer: down 106.1 -> 103.5 us, the same results
+// bit for bit), four for gate+up (unchanged at eight: 170.0 vs 169.4 us); a
+// ring of eight K steps with eight waves spills.  MXFP4 weights: eight for
+// both (T=2048 MXFP4 layer: gate+up 182 -> 166 us, down 109 -> 100 us, the
+// same results bit for bit), where four waves hold all 256 registers at one
+// wave per SIMD and eight hold 128 each at two.  MOE_STREAM_NWV (4 or 8)
+// overrides all of them for tuning runs (read once per process).
+static int stream_nwv(bool gu, bool w4)
 {
     static const int forced = [] {
         const char *e = getenv("MOE_STREAM_NWV");
         const int v = e ? atoi(e) : 0;
         return (v == 4 || v == 8) ? v : 0;
     }();
-    return forced ? forced : (gu ? 4 : 8);
+    return forced ? forced : (w4 || !gu ? 8 : 4);
 }
 
 template <int BM, bool GU, int SKC>
 static void run_skc(const ExpertArgs &a, hipStream_t st)
 {
     if constexpr (BM == 128 && SKC == 128) {
-        if (stream_nwv(GU) == 8) {
+        if (stream_nwv(GU, false) == 8) {
             if (stream_sd(BM) == 4)
                 run<BM, GU, 4, SKC, false, 1, false, 8>(a, st);
             else
@@ -930,7 +935,9 @@ static void run_sd(const ExpertArgs &a, hipStream_t st)
         return;
     }
     if (a.wdt == W_MXFP4) {  // a ring of two 128-K chunks of fp4 codes
-        if (stream_tl_w4() == 1)
+        if (BM == 128 && stream_tl_w4() == 2 && stream_nwv(GU, true) == 8)
+            run<128, GU, 2, 128, true, 2, false, 8>(a, st);
+        else if (stream_tl_w4() == 1)
             run<BM, GU, 2, 128, true, 1>(a, st);
         else
             run<BM, GU, 2, 128, true, 2>(a, st);
