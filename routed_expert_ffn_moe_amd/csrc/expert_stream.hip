@@ -898,15 +898,15 @@ static int stream_tl_w4()
 // both (T=2048 MXFP4 layer: gate+up 182 -> 166 us, down 109 -> 100 us, the
 // same results bit for bit), where four waves hold all 256 registers at one
 // wave per SIMD and eight hold 128 each at two.  MOE_STREAM_NWV (4 or 8)
-// overrides all of them for tuning runs (read once per process).
+// overrides all of them (read at each call, so that one process can compare
+// the two).
 static int stream_nwv(bool gu, bool w4)
 {
-    static const int forced = [] {
-        const char *e = getenv("MOE_STREAM_NWV");
-        const int v = e ? atoi(e) : 0;
-        return (v == 4 || v == 8) ? v : 0;
-    }();
-    return forced ? forced : (w4 || !gu ? 8 : 4);
+    const char *e = getenv("MOE_STREAM_NWV");
+    const int v = e ? atoi(e) : 0;
+    if (v == 4 || v == 8)
+        return v;
+    return w4 || !gu ? 8 : 4;
 }
 
 template <int BM, bool GU, int SKC>

@@ -562,6 +562,25 @@ def test_wide_tiles_match_narrow_tiles_bit_exactly(name, monkeypatch):
     assert torch.equal(ys[0], ys[1])
 
 
+@pytest.mark.parametrize("w", ["bf16", "mxfp4"])
+def test_eight_wave_tiles_match_four_wave_tiles_bit_exactly(w, monkeypatch):
+    """The 128-row stream tiles with four waves per workgroup and with eight
+    (each wave half the weight rows) run every output element's MFMAs over
+    the same K steps in the same order: y must not differ in a single bit,
+    for bf16 and for MXFP4 weights, in both projections."""
+    c = dict(SWEEP["SH"], w=w, layer="SH", seed=5000 + ord("H"), desc="SH")
+    lay = mi.make_layer(c, "cuda")
+    g = hx.GpuLayer(c, lay)
+    xd = hx.act_torch(hx.margin_x(c, lay), c["act"], "cuda")
+    monkeypatch.setenv("MOE_STREAM_WIDE", "0")
+    ys = []
+    for v in ("4", "8"):
+        monkeypatch.setenv("MOE_STREAM_NWV", v)
+        y, _, _ = g.forward(xd, poison=True)
+        ys.append(y.view(torch.int16).cpu())
+    assert torch.equal(ys[0], ys[1])
+
+
 def test_zero_tokens_is_a_no_op():
     c, g = layer("c1")
     xd = torch.empty((0, c["H"]), dtype=torch.bfloat16, device="cuda")
