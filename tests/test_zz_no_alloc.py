@@ -2,7 +2,7 @@
 is the library's static device array) against moe_forward on the same
 inputs: identical routing and y, on two calls in a row, the second with a
 smaller input (the scratch then holds the first call's leftovers), for the
-bf16 prefill layer and the MXFP4 decode layer.  The size refusal runs
+bf16 prefill layer and the MXFP4 layer (decode rows and prefill chunks).  The size refusal runs
 without a GPU."""
 import ctypes
 
@@ -35,11 +35,13 @@ def test_noalloc_refuses_passes_beyond_its_scratch():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("name,T1,T2", [("c1", 128, 40), ("c1", 600, 300), ("c4_t6", 6, 1)])
+@pytest.mark.parametrize("name,T1,T2", [("c1", 128, 40), ("c1", 600, 300), ("c4_t6", 6, 1),
+                                        ("c4_t6", 600, 300)])
 def test_noalloc_matches_forward_on_two_calls(name, T1, T2):
     """Short passes (T <= 128: the one-launch routing), long passes (T = 600
     and 300: the segmented router and the one-launch permutation over 5 and
-    3 blocks) and the MXFP4 decode rows."""
+    3 blocks), the MXFP4 decode rows, and MXFP4 prefill chunks (T = 600: the
+    streaming kernels' 128-row tiles; T = 300: the MXFP4 tile kernels)."""
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         pytest.skip("no GPU visible")
