@@ -792,7 +792,13 @@ bool stream_ok(const ExpertArgs &a, bool gu)
 // expert, ~26 items per CU) 4.96 -> 4.56; the 256-expert top-8 layer
 // (I=768) at T=16384 1.65 -> 1.55 and T=32768 3.07 -> 2.83, at T=8192
 // (~9 items per CU) 0.93 -> 0.95, at T=4096 (~6) 0.65 -> 0.68, at T=2048
-// with Zipf bias (64 rows per expert) 0.36 -> 0.38.  MOE_STREAM_WIDE (0 or
+// with Zipf bias (64 rows per expert) 0.36 -> 0.38.  The down projection
+// (K = I) takes them only with at least 16 K chunks per item: against the
+// eight-wave narrow down tiles, with I=768 (six chunks, where the wide
+// item's store burst of 128 rows x 512 columns weighs more than its halved
+// token bytes) narrow is faster - down us, narrow vs wide, T=8192 277 vs
+// 325, T=16384 488 vs 526, T=32768 951 vs 994 - and with I=2048 wide still
+// is (the 384-expert layer at T=8192: 1581 vs 1642).  MOE_STREAM_WIDE (0 or
 // 1) overrides the rule for tuning runs and tests; it is read at each call,
 // so a workspace sized under one setting may be refused under the other.
 static bool stream_wide(const ExpertArgs &a, bool gu)
@@ -806,6 +812,8 @@ static bool stream_wide(const ExpertArgs &a, bool gu)
         return false;
     if (forced == 1)
         return true;
+    if (!gu && a.I < 16 * 128)
+        return false;
     const int64_t pairs = (int64_t)a.shape_T * a.k;
     const int64_t tiles = pairs / 128 + a.E + (a.I_shared > 0 ? a.shape_T / 128 : 0);
     return pairs >= 128 * (int64_t)a.E &&
