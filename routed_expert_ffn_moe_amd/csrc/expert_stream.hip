@@ -832,26 +832,35 @@ int stream_ntn(const ExpertArgs &a, bool gu)
 }
 
 // Row-tile size by the mean rows per expert; MOE_STREAM_BM (16, 32, 64 or
-// 128) overrides it for tuning runs (read once per process).
+// 128) overrides it (read at each call, so that one process can compare
+// tile sizes; a workspace sized under one setting may be refused under
+// another).
 int stream_bm(const ExpertArgs &a)
 {
-    static const int forced = [] {
-        const char *e = getenv("MOE_STREAM_BM");
-        const int v = e ? atoi(e) : 0;
-        return (v == 16 || v == 32 || v == 64 || v == 128) ? v : 0;
-    }();
-    if (forced)
+    const char *e = getenv("MOE_STREAM_BM");
+    const int forced = e ? atoi(e) : 0;
+    if (forced == 16 || forced == 32 || forced == 64 || forced == 128)
         return forced;
     // Measured on the 256-expert top-8 layer (uniform routing, one chunk):
     // 16-row tiles up to 4 rows per expert on average, 32 up to 16 (T=512:
     // 436 vs 519 us with 16), 128 beyond (T=1024: 482 vs 615 us with 32 -
     // with 32-row tiles the experts a little above the mean read their
-    // weights twice).
+    // weights twice; 64-row tiles are slower at every T from 1024 to 8192,
+    // 487-895 us against 493-1129).
     const int64_t avg = (int64_t)a.shape_T * a.k / a.E;
     if (avg <= 4)
         return 16;
     if (avg <= 16)
         return 32;
+    // MXFP4 weights take a quarter of the bytes, so the two workgroups per
+    // CU of the 64-row tiles (each wave reads 64 token rows from LDS instead
+    // of the eight-wave 128-row tile's 128) win from 32 rows per expert on;
+    // 32-row tiles below that.  Measured, us per layer with 32 / 64 / 128-row
+    // tiles: T=600 159 / 171 / 216, T=1024 221 / 185 / 227, T=2048 332 / 264
+    // / 296 (Zipf-routed 289 / 234 / 296), T=4096 - / 438 / 497, T=8192 - /
+    // 756 / 795; the same results bit for bit.
+    if (a.wdt == W_MXFP4)
+        return avg <= 24 ? 32 : 64;
     return 128;
 }
 

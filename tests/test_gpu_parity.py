@@ -395,7 +395,7 @@ def test_mxfp4_path_matches_bf16_path_on_the_same_weights(T, hot):
 def test_mxfp4_prefill_chunks(T, bias):
     """MXFP4 experts in prefill chunks (more than 16 rows per expert on
     average): the streaming kernels with fp4 weights converted to bf16 in
-    registers, row tiles of 32 (T=600, 1024) and 128 (T=2048 skewed, 4096),
+    registers, row tiles of 32 (T=600) and 64 (T=1024, 2048 skewed, 4096),
     routing on every token and y on tile-edge rows of the most-loaded
     experts (all rows at T=600)."""
     say("[mxfp4 prefill] T =", T, bias)
@@ -414,7 +414,7 @@ def test_mxfp4_prefill_chunks(T, bias):
     assert np.array_equal(idx.cpu().numpy(), idx_r)
     assert np.abs(w.cpu().numpy() - w_r).max() <= hx.W_TOL
     tokens = None if T <= 600 else tile_edge_tokens(idx_r, c["E"], c["top_k"], 0,
-                                                    bm=32 if T <= 1024 else 128)
+                                                    bm=32 if T * 8 // 256 <= 24 else 64)
     experts = sorted(set((idx_r if tokens is None else idx_r[tokens]).reshape(-1).tolist()))
     y_ref, _, _ = oracle.forward(hx.oracle_layer(c, lay, experts), x, tokens)
     yh = hx.y_host(y, c["act"])
@@ -573,6 +573,7 @@ def test_eight_wave_tiles_match_four_wave_tiles_bit_exactly(w, monkeypatch):
     g = hx.GpuLayer(c, lay)
     xd = hx.act_torch(hx.margin_x(c, lay), c["act"], "cuda")
     monkeypatch.setenv("MOE_STREAM_WIDE", "0")
+    monkeypatch.setenv("MOE_STREAM_BM", "128")  # MXFP4 passes default to 64-row tiles
     ys = []
     for v in ("4", "8"):
         monkeypatch.setenv("MOE_STREAM_NWV", v)

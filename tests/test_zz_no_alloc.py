@@ -41,7 +41,7 @@ def test_noalloc_matches_forward_on_two_calls(name, T1, T2):
     """Short passes (T <= 128: the one-launch routing), long passes (T = 600
     and 300: the segmented router and the one-launch permutation over 5 and
     3 blocks), the MXFP4 decode rows, and MXFP4 prefill chunks (T = 600: the
-    streaming kernels' 128-row tiles; T = 300: the MXFP4 tile kernels)."""
+    streaming kernels' 32-row tiles; T = 300: the MXFP4 tile kernels)."""
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         pytest.skip("no GPU visible")
